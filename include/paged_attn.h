@@ -1,0 +1,220 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged grouped-query attention
+ * library: a KV cache kept in fixed 256-position pages behind a per-stream
+ * page table, with split-K decode (partials plus a log-sum-exp merge) and
+ * causal prompt-chunk prefill over the paged prefix.
+ *
+ * Sources the operations follow (TensorFold pull requests and issue):
+ *   - pull request #1373, "What changes": decode tiles and prompt rows read
+ *     key rows through the stream's page table when it has one, else from a
+ *     contiguous slab, with the same arithmetic either way;
+ *   - pull request #2011, "What this changes" and review section "Is paged
+ *     output the same as windowed output?": pages of 256 positions, the page
+ *     looked up once per page, addresses change and the bytes do not;
+ *   - pull request #2011, review section "Memory admission": pages claimed
+ *     up front, all or nothing, lowest ids for KV;
+ *   - issue #1344, "Mechanism" and "Conclusion": decode is a split partial
+ *     plus a merge, and a stream's result must not depend on what else is in
+ *     the batch (one arithmetic for paged and contiguous streams).
+ *
+ * Conventions for every entry point:
+ *   - "device" pointers point into GPU memory the caller owns; the library
+ *     never allocates, frees or synchronises device memory.  Work is enqueued
+ *     on the HIP stream passed as `hip_stream` (a hipStream_t; NULL is the
+ *     default stream) and completes asynchronously.
+ *   - Descriptor arrays (pa_kv_cache, pa_stream) are host memory and are
+ *     read only during the call.
+ *   - All validation happens on the host before anything is enqueued.  On a
+ *     negative status nothing has been launched and no output byte changed.
+ *   - A query row i of a stream is at absolute position first_pos + i and
+ *     attends keys 0 .. first_pos + i inclusive (causal).  Q and the output
+ *     are bf16 [total_rows][n_q_heads][head_dim], row-major; a stream's rows
+ *     are rows row_offset .. row_offset + n_rows - 1.  Query head h reads kv
+ *     head h / (n_q_heads / n_kv_heads).
+ *   - Page ids read from a device page table are checked on the device: an
+ *     id outside [0, n_pages) is never dereferenced; attention rows that
+ *     would read it produce NaN and write_kv skips the row.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define PA_API __attribute__((visibility("default")))
+#else
+#define PA_API
+#endif
+
+/* Positions per page; fixed at compile time in every kernel. */
+#define PA_PAGE_POSITIONS 256
+/* Default split-K size of decode, in keys (a multiple of the page). */
+#define PA_DEFAULT_SPLIT_KEYS 4096
+/* Most query rows per stream one decode call serves (verify rows). */
+#define PA_DECODE_MAX_ROWS 16
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_EINVAL = -1,        /* a null pointer, bad enum, bad count or bad shape */
+  PA_ERANGE = -2,        /* rows past the stream's context, overlapping rows */
+  PA_ENOSPC = -3,        /* page pool: not enough free pages right now */
+  PA_ETOOBIG = -4,       /* page pool: more pages than the pool will ever hold */
+  PA_EWORKSPACE = -5,    /* decode workspace missing or smaller than required */
+  PA_EDEVICE = -6,       /* a HIP launch failed (hipGetLastError after launch) */
+  PA_EUNSUPPORTED = -7   /* head_dim or group size this build has no kernel for */
+} pa_status;
+
+typedef enum pa_kv_dtype {
+  PA_KV_BF16 = 0,        /* bf16 keys and values */
+  PA_KV_FP8_E4M3 = 1     /* OCP E4M3FN codes times a per-tensor scale */
+} pa_kv_dtype;
+
+typedef enum pa_layout {
+  PA_LAYOUT_PAGED = 0,   /* rows live in pool pages named by page_table */
+  PA_LAYOUT_SLAB = 1     /* rows live in a per-stream contiguous slab */
+} pa_layout;
+
+/*
+ * The page pool as the kernels see it (one layer's pool, or one layer's
+ * block inside a multi-layer pool when page_stride is larger).
+ *
+ * K, page p, kv head g, slot j (position 256*t + j of the page's stream),
+ * dim d: element  p*page_stride + (g*256 + j)*head_dim + d        (head-major)
+ * V, same:       element  p*page_stride + (g*head_dim + d)*256 + j (transposed)
+ *
+ * Elements are bf16 (2 bytes) or E4M3FN codes (1 byte) per `dtype`.  V is
+ * stored dim-major inside a page so that the MFMA operand of P.V (eight
+ * consecutive keys of one dim) is one contiguous 16-byte load.
+ */
+typedef struct pa_kv_cache {
+  void *k_pages;         /* device, may be NULL if no stream is paged */
+  void *v_pages;         /* device, may be NULL if no stream is paged */
+  int64_t page_stride;   /* elements between pages, >= n_kv_heads*256*head_dim */
+  int32_t n_pages;       /* pages in the pool */
+  int32_t n_kv_heads;    /* >= 1 */
+  int32_t head_dim;      /* 128 or 256 */
+  int32_t dtype;         /* pa_kv_dtype */
+  float k_scale;         /* fp8: value = code * k_scale; ignored for bf16 */
+  float v_scale;         /* fp8: value = code * v_scale; ignored for bf16 */
+} pa_kv_cache;
+
+/*
+ * One stream (sequence) of a launch.  Slab layout, capacity C positions:
+ * K element (g*C + t)*head_dim + d, V element (g*head_dim + d)*C + t, same
+ * dtype as the cache.  C must be a multiple of 256.
+ */
+typedef struct pa_stream {
+  int32_t layout;          /* pa_layout */
+  int32_t ctx_len;         /* positions stored for the stream (>= 1) */
+  int32_t n_rows;          /* query rows in this call (>= 0) */
+  int32_t row_offset;      /* index of the stream's first row in q / out */
+  int32_t first_pos;       /* absolute position of the first row; first_pos + n_rows <= ctx_len */
+  int32_t reserved;        /* must be 0 */
+  const int32_t *page_table; /* device, ceil(ctx_len/256) page ids (paged layout) */
+  void *k_slab;            /* device (slab layout) */
+  void *v_slab;            /* device (slab layout) */
+  int64_t slab_cap;        /* slab capacity in positions (slab layout) */
+} pa_stream;
+
+/* Text for a pa_status value (static storage). */
+PA_API const char *pa_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+PA_API int pa_version(void);
+
+/* ---------------------------------------------------------------- page pool
+ * Host-side bookkeeping of which page ids are free (pull request #2011,
+ * "Memory admission").  The pool's device memory is the caller's.  A pool
+ * handle is not thread-safe; serialise calls on one handle. */
+typedef struct pa_page_pool pa_page_pool;
+
+/* Create a pool of n_pages free pages (ids 0..n_pages-1).  *out receives the
+ * handle.  PA_EINVAL if n_pages < 1 or out is NULL. */
+PA_API int page_pool_create(int32_t n_pages, pa_page_pool **out);
+
+/* Release the handle (NULL is allowed). */
+PA_API void page_pool_destroy(pa_page_pool *pool);
+
+/* Claim n pages, all or nothing, lowest free ids first, written in
+ * ascending order to ids_out (host, n entries).  PA_ETOOBIG if n exceeds the
+ * pool's size (it can never fit), PA_ENOSPC if fewer than n are free now
+ * (nothing is claimed), PA_EINVAL for n < 0 or null pointers. */
+PA_API int page_pool_alloc(pa_page_pool *pool, int32_t n, int32_t *ids_out);
+
+/* Return n pages.  PA_ERANGE if an id is out of range or not currently
+ * claimed (nothing is freed in that case). */
+PA_API int page_pool_free(pa_page_pool *pool, const int32_t *ids, int32_t n);
+
+/* Number of free pages, or a negative status for a NULL pool. */
+PA_API int32_t page_pool_free_count(const pa_page_pool *pool);
+
+/* ----------------------------------------------------------------- write_kv
+ * Store new key/value rows (the step the pages call the rope stores, with
+ * RoPE already applied by the caller): for each stream, rows
+ * row_offset .. row_offset+n_rows-1 of k_new / v_new (bf16, device,
+ * [total_rows][n_kv_heads][head_dim]) go to positions first_pos .. of the
+ * stream, through its page table or into its slab.  fp8 caches quantise
+ * each element as RNE_E4M3FN(clamp(fl32(x) / scale, -448, 448)) (NaN stays
+ * NaN).  Streams must not write the same position twice in one call. */
+PA_API int write_kv(const pa_kv_cache *cache, const pa_stream *streams, int32_t n_streams,
+             const void *k_new, const void *v_new, void *hip_stream);
+
+/* ----------------------------------------------------------------- decode
+ * Split-K decode (issue #1344, "Mechanism"): each stream's keys
+ * 0 .. first_pos+n_rows-1 are cut into splits of split_keys keys from
+ * position 0; one partial (m, l, o) per (row, q head, split) is written to
+ * the workspace, then a fixed-order log-sum-exp merge writes
+ * out = v_scale * sum_j e^(m_j-M) o_j / sum_j e^(m_j-M) l_j  as bf16 (RNE).
+ * The split count of a stream depends on that stream alone, so a stream's
+ * output bytes do not depend on the other streams in the call.
+ * n_rows per stream <= PA_DECODE_MAX_ROWS; sm_scale > 0 (1/sqrt(head_dim)
+ * is the usual value); split_keys a positive multiple of 256.
+ * The workspace (device, >= paged_attn_decode_workspace_size bytes, 256-byte
+ * aligned) holds the partials; it is fully overwritten before it is read. */
+PA_API size_t paged_attn_decode_workspace_size(const pa_stream *streams, int32_t n_streams,
+                                        int32_t n_q_heads, int32_t head_dim, int32_t split_keys);
+
+PA_API int paged_attn_decode(const pa_kv_cache *cache, const pa_stream *streams, int32_t n_streams,
+                      const void *q, void *out, int32_t n_q_heads, float sm_scale,
+                      int32_t split_keys, void *workspace, size_t workspace_bytes,
+                      void *hip_stream);
+
+/* Launch plan of a decode call, for callers that size grids or check
+ * scheduling: per stream its split count (splits_out, n_streams entries, may
+ * be NULL), and the totals.  Host only; validates like paged_attn_decode
+ * minus the device pointers. */
+typedef struct pa_decode_plan {
+  int32_t n_launch_groups;   /* kernel pairs enqueued (streams are grouped) */
+  int32_t total_splits;      /* sum over streams of their split counts */
+  int32_t col_tiles;         /* 16-column MFMA tiles per (split, kv head) */
+  int32_t partial_blocks;    /* workgroups of the partial kernel(s) */
+  int32_t merge_blocks;      /* workgroups of the merge kernel(s) */
+  int32_t reserved;
+  size_t workspace_bytes;
+} pa_decode_plan;
+
+PA_API int paged_attn_decode_plan(const pa_stream *streams, int32_t n_streams, int32_t n_q_heads,
+                           int32_t n_kv_heads, int32_t head_dim, int32_t split_keys,
+                           int32_t *splits_out, pa_decode_plan *plan);
+
+/* ----------------------------------------------------------------- prefill
+ * Prompt-chunk prefill (pull request #1373, prompt rows; pull request #2011,
+ * hpattn_p256_kernel): every row of every stream, causal against the
+ * stream's stored prefix, one launch, page size 256 fixed.  Rows are tiled
+ * 128 at a time within a stream (tiles never span streams); a row's bytes do
+ * not depend on which other rows share its tile, so any slicing of a
+ * stream's rows into calls gives the same bytes as one call. */
+PA_API int paged_attn_prefill(const pa_kv_cache *cache, const pa_stream *streams, int32_t n_streams,
+                       const void *q, void *out, int32_t n_q_heads, float sm_scale,
+                       void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,324 @@
+"""Python binding of the gfx950 paged grouped-query attention library.
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels of ``libpaged_attn.so`` (see ``include/paged_attn.h``).  PyTorch
+provides device memory and streams.  There is no fallback: if the shared
+library is missing, every compute call raises.
+
+Entry points carry the C names: ``page_pool_create`` / ``page_pool_alloc`` /
+``page_pool_free`` / ``page_pool_destroy`` / ``page_pool_free_count``,
+``write_kv``, ``paged_attn_decode_workspace_size``, ``paged_attn_decode``,
+``paged_attn_decode_plan``, ``paged_attn_prefill``, ``pa_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
+
+PAGE_POSITIONS = 256
+DEFAULT_SPLIT_KEYS = 4096
+DECODE_MAX_ROWS = 16
+
+PA_OK, PA_EINVAL, PA_ERANGE, PA_ENOSPC, PA_ETOOBIG, PA_EWORKSPACE, PA_EDEVICE, PA_EUNSUPPORTED = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+PA_KV_BF16, PA_KV_FP8_E4M3 = 0, 1
+PA_LAYOUT_PAGED, PA_LAYOUT_SLAB = 0, 1
+
+EXPORTS = ["pa_status_string", "pa_version", "page_pool_create", "page_pool_destroy",
+           "page_pool_alloc", "page_pool_free", "page_pool_free_count", "write_kv",
+           "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_plan",
+           "paged_attn_prefill"]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class pa_kv_cache(C.Structure):
+    _fields_ = [("k_pages", C.c_void_p), ("v_pages", C.c_void_p), ("page_stride", C.c_int64),
+                ("n_pages", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float)]
+
+
+class pa_stream(C.Structure):
+    _fields_ = [("layout", C.c_int32), ("ctx_len", C.c_int32), ("n_rows", C.c_int32),
+                ("row_offset", C.c_int32), ("first_pos", C.c_int32), ("reserved", C.c_int32),
+                ("page_table", C.c_void_p), ("k_slab", C.c_void_p), ("v_slab", C.c_void_p),
+                ("slab_cap", C.c_int64)]
+
+
+class pa_decode_plan(C.Structure):
+    _fields_ = [("n_launch_groups", C.c_int32), ("total_splits", C.c_int32),
+                ("col_tiles", C.c_int32), ("partial_blocks", C.c_int32),
+                ("merge_blocks", C.c_int32), ("reserved", C.c_int32),
+                ("workspace_bytes", C.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run __graft_entry__.build())")
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+        L.pa_status_string.restype = C.c_char_p
+        L.pa_status_string.argtypes = [C.c_int]
+        L.pa_version.restype = C.c_int
+        L.pa_version.argtypes = []
+        L.page_pool_create.restype = C.c_int
+        L.page_pool_create.argtypes = [i32, C.POINTER(P)]
+        L.page_pool_destroy.restype = None
+        L.page_pool_destroy.argtypes = [P]
+        L.page_pool_alloc.restype = C.c_int
+        L.page_pool_alloc.argtypes = [P, i32, P]
+        L.page_pool_free.restype = C.c_int
+        L.page_pool_free.argtypes = [P, P, i32]
+        L.page_pool_free_count.restype = i32
+        L.page_pool_free_count.argtypes = [P]
+        L.write_kv.restype = C.c_int
+        L.write_kv.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream), i32, P, P, P]
+        L.paged_attn_decode_workspace_size.restype = sz
+        L.paged_attn_decode_workspace_size.argtypes = [C.POINTER(pa_stream), i32, i32, i32, i32]
+        L.paged_attn_decode.restype = C.c_int
+        L.paged_attn_decode.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream), i32, P, P,
+                                        i32, f32, i32, P, sz, P]
+        L.paged_attn_decode_plan.restype = C.c_int
+        L.paged_attn_decode_plan.argtypes = [C.POINTER(pa_stream), i32, i32, i32, i32, i32, P,
+                                             C.POINTER(pa_decode_plan)]
+        L.paged_attn_prefill.restype = C.c_int
+        L.paged_attn_prefill.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream), i32, P, P,
+                                         i32, f32, P]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pa_status_string(int(status)).decode()
+
+
+pa_status_string = status_string
+
+
+def _check(rc: int, what: str):
+    if rc != PA_OK:
+        raise PagedAttnError(rc, what)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _hip_stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+# ----------------------------------------------------------------------------- descriptors
+
+@dataclass
+class KVCache:
+    """Device pool tensors plus geometry; see pa_kv_cache in paged_attn.h.
+
+    K page layout [n_pages][Hkv][256][D]; V page layout [n_pages][Hkv][D][256].
+    dtype: "bf16" (torch.bfloat16 storage) or "fp8" (uint8 E4M3FN codes).
+    """
+    k_pages: object
+    v_pages: object
+    n_pages: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str = "bf16"
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    page_stride: int | None = None
+
+    def c(self) -> pa_kv_cache:
+        ps = self.page_stride or self.n_kv_heads * PAGE_POSITIONS * self.head_dim
+        return pa_kv_cache(_ptr(self.k_pages), _ptr(self.v_pages), ps, self.n_pages,
+                           self.n_kv_heads, self.head_dim,
+                           PA_KV_BF16 if self.dtype == "bf16" else PA_KV_FP8_E4M3,
+                           float(self.k_scale), float(self.v_scale))
+
+
+@dataclass
+class Stream:
+    """One stream of a call; see pa_stream in paged_attn.h."""
+    ctx_len: int
+    n_rows: int
+    row_offset: int
+    first_pos: int
+    page_table: object = None     # torch.int32 device tensor (paged)
+    k_slab: object = None         # device tensor [Hkv][cap][D]
+    v_slab: object = None         # device tensor [Hkv][D][cap]
+    slab_cap: int = 0
+    layout: int = PA_LAYOUT_PAGED
+
+    def c(self) -> pa_stream:
+        return pa_stream(int(self.layout), int(self.ctx_len), int(self.n_rows),
+                         int(self.row_offset), int(self.first_pos), 0, _ptr(self.page_table),
+                         _ptr(self.k_slab), _ptr(self.v_slab), int(self.slab_cap))
+
+
+def _streams(streams):
+    arr = (pa_stream * max(len(streams), 1))()
+    for i, s in enumerate(streams):
+        arr[i] = s.c() if isinstance(s, Stream) else s
+    return arr, len(streams)
+
+
+def alloc_pool(n_pages: int, n_kv_heads: int, head_dim: int, dtype: str = "bf16",
+               device="cuda", zero: bool = True) -> KVCache:
+    """Allocate pool tensors on the device (torch memory, caller-owned)."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.uint8
+    mk = torch.zeros if zero else torch.empty
+    k = mk((n_pages, n_kv_heads, PAGE_POSITIONS, head_dim), dtype=tdt, device=device)
+    v = mk((n_pages, n_kv_heads, head_dim, PAGE_POSITIONS), dtype=tdt, device=device)
+    return KVCache(k, v, n_pages, n_kv_heads, head_dim, dtype)
+
+
+def alloc_slab(cap: int, n_kv_heads: int, head_dim: int, dtype: str = "bf16", device="cuda",
+               zero: bool = True):
+    """Slab tensors K [Hkv][cap][D] and V [Hkv][D][cap]; cap a multiple of 256."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.uint8
+    mk = torch.zeros if zero else torch.empty
+    return (mk((n_kv_heads, cap, head_dim), dtype=tdt, device=device),
+            mk((n_kv_heads, head_dim, cap), dtype=tdt, device=device))
+
+
+# ----------------------------------------------------------------------------- page pool
+
+class PagePool:
+    """Host bookkeeping of free page ids (page_pool_* in paged_attn.h)."""
+
+    def __init__(self, n_pages: int):
+        h = C.c_void_p()
+        _check(lib().page_pool_create(int(n_pages), C.byref(h)), "page_pool_create")
+        self._h = h
+        self.n_pages = n_pages
+
+    def alloc(self, n: int) -> np.ndarray:
+        ids = np.empty(max(n, 1), np.int32)
+        _check(lib().page_pool_alloc(self._h, int(n), ids.ctypes.data_as(C.c_void_p)),
+               "page_pool_alloc")
+        return ids[:n]
+
+    def free(self, ids) -> None:
+        a = np.ascontiguousarray(ids, np.int32)
+        _check(lib().page_pool_free(self._h, a.ctypes.data_as(C.c_void_p), len(a)),
+               "page_pool_free")
+
+    def free_count(self) -> int:
+        return int(lib().page_pool_free_count(self._h))
+
+    def close(self):
+        if self._h:
+            lib().page_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def page_pool_create(n_pages: int) -> PagePool:
+    return PagePool(n_pages)
+
+
+def page_pool_alloc(pool: PagePool, n: int) -> np.ndarray:
+    return pool.alloc(n)
+
+
+def page_pool_free(pool: PagePool, ids) -> None:
+    pool.free(ids)
+
+
+def page_pool_free_count(pool: PagePool) -> int:
+    return pool.free_count()
+
+
+def page_pool_destroy(pool: PagePool) -> None:
+    pool.close()
+
+
+# ----------------------------------------------------------------------------- kernels
+
+def write_kv(cache: KVCache, streams, k_new, v_new, stream=None) -> None:
+    """Store bf16 rows [rows][Hkv][D] at each stream's positions first_pos.."""
+    arr, n = _streams(streams)
+    cc = cache.c()
+    _check(lib().write_kv(C.byref(cc), arr, n, _ptr(k_new), _ptr(v_new), _hip_stream(stream)),
+           "write_kv")
+
+
+def paged_attn_decode_workspace_size(streams, n_q_heads: int, head_dim: int,
+                                     split_keys: int = DEFAULT_SPLIT_KEYS) -> int:
+    arr, n = _streams(streams)
+    return int(lib().paged_attn_decode_workspace_size(arr, n, int(n_q_heads), int(head_dim),
+                                                      int(split_keys)))
+
+
+def paged_attn_decode_plan(streams, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                           split_keys: int = DEFAULT_SPLIT_KEYS):
+    """(per-stream split counts, pa_decode_plan) without launching anything."""
+    arr, n = _streams(streams)
+    splits = np.zeros(max(n, 1), np.int32)
+    plan = pa_decode_plan()
+    _check(lib().paged_attn_decode_plan(arr, n, int(n_q_heads), int(n_kv_heads), int(head_dim),
+                                        int(split_keys), splits.ctypes.data_as(C.c_void_p),
+                                        C.byref(plan)), "paged_attn_decode_plan")
+    return splits[:n], plan
+
+
+def paged_attn_decode(cache: KVCache, streams, q, out=None, sm_scale: float | None = None,
+                      split_keys: int = DEFAULT_SPLIT_KEYS, workspace=None, stream=None):
+    """Split-K decode; q/out bf16 [rows][Hq][D]. Returns out."""
+    import torch
+    n_q_heads = int(q.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    if sm_scale is None:
+        sm_scale = cache.head_dim ** -0.5
+    arr, n = _streams(streams)
+    if workspace is None:
+        nb = int(lib().paged_attn_decode_workspace_size(arr, n, n_q_heads, cache.head_dim,
+                                                        int(split_keys)))
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+    cc = cache.c()
+    _check(lib().paged_attn_decode(C.byref(cc), arr, n, _ptr(q), _ptr(out), n_q_heads,
+                                   float(sm_scale), int(split_keys), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _hip_stream(stream)), "paged_attn_decode")
+    return out
+
+
+def paged_attn_prefill(cache: KVCache, streams, q, out=None, sm_scale: float | None = None,
+                       stream=None):
+    """Causal prefill of every row of every stream; q/out bf16 [rows][Hq][D]."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    if sm_scale is None:
+        sm_scale = cache.head_dim ** -0.5
+    arr, n = _streams(streams)
+    cc = cache.c()
+    _check(lib().paged_attn_prefill(C.byref(cc), arr, n, _ptr(q), _ptr(out), int(q.shape[1]),
+                                    float(sm_scale), _hip_stream(stream)), "paged_attn_prefill")
+    return out

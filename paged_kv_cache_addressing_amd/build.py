@@ -1,0 +1,53 @@
+"""Build the gfx950 paged-attention library (libpaged_attn.so) with hipcc.
+
+Every kernel is compiled for gfx950 only, with packed-fp32 instruction
+selection switched off and IEEE-correct fp32 division (the fp8 store
+quantiser divides).  The library is built in-tree next to this file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libpaged_attn.so")
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "write_kv.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "--offload-arch=gfx950",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Wall", "-Wno-unused-function",
+    "-I" + os.path.join(ROOT, "include"),
+]
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> str:
+    """Compile and link; returns the path of the shared library."""
+    objs = []
+    os.makedirs(os.path.join(HERE, "_build"), exist_ok=True)
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(HERE, "_build", src + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [HIPCC] + COMMON + lang + ["-c", path, "-o", obj]
+        if resource_usage and src.endswith(".hip"):
+            cmd += ["-Rpass-analysis=kernel-resource-usage"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True, resource_usage="--usage" in sys.argv))

@@ -1,0 +1,398 @@
+// C ABI of the paged attention library: argument validation, split and tile
+// planning, launch grouping, and the host-side page pool.  Every check runs
+// before anything is enqueued; a failed call launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "../../include/paged_attn.h"
+#include "pa_internal.hpp"
+
+namespace {
+
+using pa::kMaxLaunchStreams;
+using pa::kPage;
+using pa::kPrefillRows;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool paged_any(const pa_stream* s, int32_t n) {
+  for (int32_t i = 0; i < n; ++i)
+    if (s[i].layout == PA_LAYOUT_PAGED && s[i].n_rows > 0) return true;
+  return false;
+}
+
+// Shape checks that need no device pointer.
+int check_streams_shape(const pa_stream* s, int32_t n, int32_t n_q_heads, int32_t n_kv_heads,
+                        int32_t head_dim, int max_rows) {
+  if (n < 0) return PA_EINVAL;
+  if (n > 0 && !s) return PA_EINVAL;
+  if (n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads != 0) return PA_EINVAL;
+  if (head_dim != 128 && head_dim != 256) return PA_EUNSUPPORTED;
+  std::vector<std::pair<int64_t, int64_t>> spans;
+  spans.reserve((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const pa_stream& t = s[i];
+    if (t.layout != PA_LAYOUT_PAGED && t.layout != PA_LAYOUT_SLAB) return PA_EINVAL;
+    if (t.reserved != 0) return PA_EINVAL;
+    if (t.ctx_len < 1 || t.n_rows < 0 || t.first_pos < 0 || t.row_offset < 0) return PA_EINVAL;
+    if ((int64_t)t.first_pos + t.n_rows > t.ctx_len) return PA_ERANGE;
+    if (max_rows > 0 && t.n_rows > max_rows) return PA_EINVAL;
+    if (t.n_rows > 0) spans.emplace_back(t.row_offset, (int64_t)t.row_offset + t.n_rows);
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].second) return PA_ERANGE;
+  return PA_OK;
+}
+
+int check_call(const pa_kv_cache* c, const pa_stream* s, int32_t n, int32_t n_q_heads,
+               int max_rows) {
+  if (!c) return PA_EINVAL;
+  if (c->dtype != PA_KV_BF16 && c->dtype != PA_KV_FP8_E4M3) return PA_EINVAL;
+  int rc = check_streams_shape(s, n, n_q_heads, c->n_kv_heads, c->head_dim, max_rows);
+  if (rc != PA_OK) return rc;
+  if (c->dtype == PA_KV_FP8_E4M3) {
+    if (!(std::isfinite(c->k_scale) && c->k_scale > 0.f)) return PA_EINVAL;
+    if (!(std::isfinite(c->v_scale) && c->v_scale > 0.f)) return PA_EINVAL;
+  }
+  if (paged_any(s, n)) {
+    if (!c->k_pages || !c->v_pages || c->n_pages < 1) return PA_EINVAL;
+    if (c->page_stride < (int64_t)c->n_kv_heads * kPage * c->head_dim) return PA_EINVAL;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const pa_stream& t = s[i];
+    if (t.n_rows == 0) continue;
+    if (t.layout == PA_LAYOUT_PAGED) {
+      if (!t.page_table) return PA_EINVAL;
+    } else {
+      if (!t.k_slab || !t.v_slab) return PA_EINVAL;
+      if (t.slab_cap < t.ctx_len || t.slab_cap % kPage != 0) return PA_EINVAL;
+    }
+  }
+  return PA_OK;
+}
+
+pa::StreamArg stream_arg(const pa_kv_cache* c, const pa_stream& t) {
+  pa::StreamArg a;
+  std::memset(&a, 0, sizeof a);
+  a.layout = t.layout;
+  a.n_rows = t.n_rows;
+  a.row_offset = t.row_offset;
+  a.first_pos = t.first_pos;
+  a.n_keys = t.first_pos + t.n_rows;
+  a.page_table = t.page_table;
+  if (t.layout == PA_LAYOUT_PAGED) {
+    a.k_base = static_cast<uint8_t*>(c ? c->k_pages : nullptr);
+    a.v_base = static_cast<uint8_t*>(c ? c->v_pages : nullptr);
+  } else {
+    a.k_base = static_cast<uint8_t*>(t.k_slab);
+    a.v_base = static_cast<uint8_t*>(t.v_slab);
+    a.slab_cap = t.slab_cap;
+  }
+  return a;
+}
+
+pa::CacheArg cache_arg(const pa_kv_cache* c) {
+  pa::CacheArg a;
+  a.page_stride = c->page_stride;
+  a.n_pages = c->n_pages;
+  a.n_kv_heads = c->n_kv_heads;
+  return a;
+}
+
+int32_t splits_of(const pa_stream& t, int32_t split_keys) {
+  if (t.n_rows == 0) return 0;
+  const int64_t nk = (int64_t)t.first_pos + t.n_rows;
+  return (int32_t)((nk + split_keys - 1) / split_keys);
+}
+
+// The decode plan: stream order is kept; streams with rows are packed into
+// launch groups of at most kMaxLaunchStreams.
+struct DecodePlan {
+  std::vector<int32_t> splits;
+  std::vector<int64_t> slot_base;
+  int64_t total_slots = 0;
+  std::vector<std::vector<int32_t>> groups;
+};
+
+int plan_decode(const pa_stream* s, int32_t n, int32_t n_q_heads, int32_t split_keys,
+                DecodePlan& P) {
+  if (split_keys < kPage || split_keys % kPage != 0) return PA_EINVAL;
+  P.splits.assign((size_t)n, 0);
+  P.slot_base.assign((size_t)n, 0);
+  P.total_slots = 0;
+  P.groups.clear();
+  for (int32_t i = 0; i < n; ++i) {
+    P.splits[i] = splits_of(s[i], split_keys);
+    P.slot_base[i] = P.total_slots;
+    P.total_slots += (int64_t)s[i].n_rows * n_q_heads * P.splits[i];
+    if (s[i].n_rows == 0) continue;
+    if (P.groups.empty() || (int)P.groups.back().size() == kMaxLaunchStreams)
+      P.groups.emplace_back();
+    P.groups.back().push_back(i);
+  }
+  return PA_OK;
+}
+
+size_t ws_bytes(int64_t total_slots, int32_t head_dim) {
+  return align256((size_t)total_slots * head_dim * sizeof(float)) +
+         align256((size_t)total_slots * 2 * sizeof(float));
+}
+
+int32_t col_tiles_of(const pa_stream* s, const std::vector<int32_t>& grp, int32_t group) {
+  int32_t mr = 0;
+  for (int32_t i : grp) mr = std::max(mr, s[i].n_rows);
+  return (group * mr + 15) / 16;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+
+struct pa_page_pool {
+  int32_t n_pages;
+  int32_t n_free;
+  std::vector<uint8_t> used;
+};
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument";
+    case PA_ERANGE: return "rows out of range or overlapping";
+    case PA_ENOSPC: return "not enough free pages";
+    case PA_ETOOBIG: return "request larger than the page pool";
+    case PA_EWORKSPACE: return "decode workspace missing or too small";
+    case PA_EDEVICE: return "HIP launch failed";
+    case PA_EUNSUPPORTED: return "unsupported head_dim";
+    default: return "unknown status";
+  }
+}
+
+int pa_version(void) { return (1 << 16) | 0; }
+
+int page_pool_create(int32_t n_pages, pa_page_pool** out) {
+  if (!out || n_pages < 1) return PA_EINVAL;
+  *out = nullptr;
+  pa_page_pool* p = new (std::nothrow) pa_page_pool;
+  if (!p) return PA_EINVAL;
+  try {
+    p->used.assign((size_t)n_pages, 0);
+  } catch (...) {
+    delete p;
+    return PA_EINVAL;
+  }
+  p->n_pages = n_pages;
+  p->n_free = n_pages;
+  *out = p;
+  return PA_OK;
+}
+
+void page_pool_destroy(pa_page_pool* pool) { delete pool; }
+
+int page_pool_alloc(pa_page_pool* pool, int32_t n, int32_t* ids_out) {
+  if (!pool || n < 0 || (n > 0 && !ids_out)) return PA_EINVAL;
+  if (n > pool->n_pages) return PA_ETOOBIG;
+  if (n > pool->n_free) return PA_ENOSPC;
+  int32_t k = 0;
+  for (int32_t id = 0; id < pool->n_pages && k < n; ++id)
+    if (!pool->used[id]) {
+      pool->used[id] = 1;
+      ids_out[k++] = id;
+    }
+  pool->n_free -= k;
+  return PA_OK;
+}
+
+int page_pool_free(pa_page_pool* pool, const int32_t* ids, int32_t n) {
+  if (!pool || n < 0 || (n > 0 && !ids)) return PA_EINVAL;
+  std::vector<int32_t> v(ids, ids + n);
+  std::sort(v.begin(), v.end());
+  for (int32_t i = 0; i < n; ++i) {
+    if (v[i] < 0 || v[i] >= pool->n_pages || !pool->used[v[i]]) return PA_ERANGE;
+    if (i > 0 && v[i] == v[i - 1]) return PA_ERANGE;
+  }
+  for (int32_t id : v) pool->used[id] = 0;
+  pool->n_free += n;
+  return PA_OK;
+}
+
+int32_t page_pool_free_count(const pa_page_pool* pool) { return pool ? pool->n_free : PA_EINVAL; }
+
+// ---------------------------------------------------------------------------
+
+int write_kv(const pa_kv_cache* cache, const pa_stream* streams, int32_t n_streams,
+             const void* k_new, const void* v_new, void* hip_stream) {
+  int rc = check_call(cache, streams, n_streams, cache ? cache->n_kv_heads : 1, 0);
+  if (rc != PA_OK) return rc;
+  bool any = false;
+  for (int32_t i = 0; i < n_streams; ++i) any |= streams[i].n_rows > 0;
+  if (!any) return PA_OK;
+  if (!k_new || !v_new) return PA_EINVAL;
+  std::vector<int32_t> live;
+  for (int32_t i = 0; i < n_streams; ++i)
+    if (streams[i].n_rows > 0) live.push_back(i);
+  for (size_t at = 0; at < live.size(); at += kMaxLaunchStreams) {
+    pa::WriteArgs A;
+    std::memset(&A, 0, sizeof A);
+    A.k_new = static_cast<const uint16_t*>(k_new);
+    A.v_new = static_cast<const uint16_t*>(v_new);
+    A.cache = cache_arg(cache);
+    A.k_scale = cache->dtype == PA_KV_FP8_E4M3 ? cache->k_scale : 1.f;
+    A.v_scale = cache->dtype == PA_KV_FP8_E4M3 ? cache->v_scale : 1.f;
+    int32_t rows = 0;
+    for (size_t j = at; j < live.size() && j < at + kMaxLaunchStreams; ++j) {
+      pa::StreamArg a = stream_arg(cache, streams[live[j]]);
+      a.row_begin = rows;
+      rows += a.n_rows;
+      A.s[A.n_streams++] = a;
+    }
+    A.total_rows = rows;
+    rc = pa::launch_write_kv(A, cache->dtype, cache->head_dim, (hipStream_t)hip_stream);
+    if (rc != 0) return rc;
+  }
+  return PA_OK;
+}
+
+size_t paged_attn_decode_workspace_size(const pa_stream* streams, int32_t n_streams,
+                                        int32_t n_q_heads, int32_t head_dim,
+                                        int32_t split_keys) {
+  if (n_streams < 0 || (n_streams > 0 && !streams) || n_q_heads < 1) return 0;
+  DecodePlan P;
+  if (plan_decode(streams, n_streams, n_q_heads, split_keys, P) != PA_OK) return 0;
+  return ws_bytes(P.total_slots, head_dim);
+}
+
+int paged_attn_decode_plan(const pa_stream* streams, int32_t n_streams, int32_t n_q_heads,
+                           int32_t n_kv_heads, int32_t head_dim, int32_t split_keys,
+                           int32_t* splits_out, pa_decode_plan* plan) {
+  int rc = check_streams_shape(streams, n_streams, n_q_heads, n_kv_heads, head_dim,
+                               PA_DECODE_MAX_ROWS);
+  if (rc != PA_OK) return rc;
+  DecodePlan P;
+  rc = plan_decode(streams, n_streams, n_q_heads, split_keys, P);
+  if (rc != PA_OK) return rc;
+  if (splits_out)
+    for (int32_t i = 0; i < n_streams; ++i) splits_out[i] = P.splits[i];
+  if (plan) {
+    std::memset(plan, 0, sizeof *plan);
+    const int32_t group = n_q_heads / n_kv_heads;
+    plan->n_launch_groups = (int32_t)P.groups.size();
+    for (const auto& grp : P.groups) {
+      int32_t ts = 0, tr = 0;
+      for (int32_t i : grp) {
+        ts += P.splits[i];
+        tr += streams[i].n_rows;
+      }
+      const int32_t ct = col_tiles_of(streams, grp, group);
+      plan->total_splits += ts;
+      plan->col_tiles = std::max(plan->col_tiles, ct);
+      plan->partial_blocks += ts * ct * n_kv_heads;
+      plan->merge_blocks += tr * n_q_heads;
+    }
+    plan->workspace_bytes = ws_bytes(P.total_slots, head_dim);
+  }
+  return PA_OK;
+}
+
+int paged_attn_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n_streams,
+                      const void* q, void* out, int32_t n_q_heads, float sm_scale,
+                      int32_t split_keys, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  int rc = check_call(cache, streams, n_streams, n_q_heads, PA_DECODE_MAX_ROWS);
+  if (rc != PA_OK) return rc;
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f)) return PA_EINVAL;
+  DecodePlan P;
+  rc = plan_decode(streams, n_streams, n_q_heads, split_keys, P);
+  if (rc != PA_OK) return rc;
+  if (P.groups.empty()) return PA_OK;
+  if (!q || !out) return PA_EINVAL;
+  const size_t need = ws_bytes(P.total_slots, cache->head_dim);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return PA_EWORKSPACE;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                          align256((size_t)P.total_slots * cache->head_dim *
+                                                   sizeof(float)));
+  const int32_t group = n_q_heads / cache->n_kv_heads;
+  const float ks = cache->dtype == PA_KV_FP8_E4M3 ? cache->k_scale : 1.f;
+  for (const auto& grp : P.groups) {
+    pa::DecodeArgs A;
+    std::memset(&A, 0, sizeof A);
+    A.q = static_cast<const uint16_t*>(q);
+    A.out = static_cast<uint16_t*>(out);
+    A.ws_o = ws_o;
+    A.ws_ml = ws_ml;
+    A.cache = cache_arg(cache);
+    A.n_q_heads = n_q_heads;
+    A.group = group;
+    A.split_keys = split_keys;
+    A.scale_log2 = sm_scale * ks * kLog2e;
+    A.v_scale = cache->dtype == PA_KV_FP8_E4M3 ? cache->v_scale : 1.f;
+    A.col_tiles = col_tiles_of(streams, grp, group);
+    int32_t splits = 0, rows = 0;
+    for (int32_t i : grp) {
+      pa::StreamArg a = stream_arg(cache, streams[i]);
+      a.n_splits = P.splits[i];
+      a.block_begin = splits;
+      a.row_begin = rows;
+      a.slot_base = P.slot_base[i];
+      splits += a.n_splits;
+      rows += a.n_rows;
+      A.s[A.n_streams++] = a;
+    }
+    A.total_splits = splits;
+    A.total_rows = rows;
+    rc = pa::launch_decode(A, cache->dtype, cache->head_dim, cache->n_kv_heads,
+                           (hipStream_t)hip_stream);
+    if (rc != 0) return rc;
+  }
+  return PA_OK;
+}
+
+int paged_attn_prefill(const pa_kv_cache* cache, const pa_stream* streams, int32_t n_streams,
+                       const void* q, void* out, int32_t n_q_heads, float sm_scale,
+                       void* hip_stream) {
+  int rc = check_call(cache, streams, n_streams, n_q_heads, 0);
+  if (rc != PA_OK) return rc;
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f)) return PA_EINVAL;
+  std::vector<int32_t> live;
+  for (int32_t i = 0; i < n_streams; ++i)
+    if (streams[i].n_rows > 0) live.push_back(i);
+  if (live.empty()) return PA_OK;
+  if (!q || !out) return PA_EINVAL;
+  const float ks = cache->dtype == PA_KV_FP8_E4M3 ? cache->k_scale : 1.f;
+  for (size_t at = 0; at < live.size(); at += kMaxLaunchStreams) {
+    pa::PrefillArgs A;
+    std::memset(&A, 0, sizeof A);
+    A.q = static_cast<const uint16_t*>(q);
+    A.out = static_cast<uint16_t*>(out);
+    A.cache = cache_arg(cache);
+    A.n_q_heads = n_q_heads;
+    A.group = n_q_heads / cache->n_kv_heads;
+    A.scale_log2 = sm_scale * ks * kLog2e;
+    A.v_scale = cache->dtype == PA_KV_FP8_E4M3 ? cache->v_scale : 1.f;
+    int32_t tiles = 0;
+    for (size_t j = at; j < live.size() && j < at + kMaxLaunchStreams; ++j) {
+      pa::StreamArg a = stream_arg(cache, streams[live[j]]);
+      a.block_begin = tiles;
+      tiles += (a.n_rows + kPrefillRows - 1) / kPrefillRows;
+      A.s[A.n_streams++] = a;
+    }
+    A.total_tiles = tiles;
+    rc = pa::launch_prefill(A, cache->dtype, cache->head_dim, (hipStream_t)hip_stream);
+    if (rc != 0) return rc;
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,291 @@
+// Split-K paged decode for gfx950: partial kernel (MFMA) + log-sum-exp merge.
+//
+// Decode is a split partial followed by a merge (TensorFold issue #1344,
+// "Mechanism"); the decode tiles read key rows through the page table, one
+// lookup per page (pull request #2011, "What this changes").  One workgroup
+// owns one (stream, 4096-key split, kv head, 16-column tile); its four waves
+// take the split's pages round-robin and are combined in fixed wave order,
+// so the partial of a split depends on that split's keys and queries alone.
+//
+// MFMA mapping (v_mfma_f32_16x16x32_bf16, wave64):
+//   S^T = K Q^T : A = 16 keys x 32 dims of K, B = 32 dims x 16 columns of Q^T,
+//                 a column being one (query row, q head of the group).
+//   O^T += V^T P^T : A = 16 dims x 32 keys of V^T (V is dim-major inside a
+//                 page, so a lane's 8 keys are one 16-byte load), B = P^T.
+// The keys of each S^T m-tile are permuted so that the C-layout rows a lane
+// ends up holding are exactly the 8 consecutive keys its P^T operand needs:
+// no data moves between the two products.  K and V go straight from HBM to
+// registers: with one column tile no operand is shared across waves, so
+// staging through LDS would add latency and no reuse.
+#include "pa_device.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+
+// First dim of the 8-dim run a lane of lane-group `a` holds at QK k-step ks.
+// bf16: natural order.  fp8: two k-steps share one 16-byte load, so the run
+// for (ks, a) is dims 64*(ks/2) + 16a + 8*(ks%2) .. +7.  Q^T follows the same
+// permutation, so the dot product is unchanged.
+template <int KV>
+__device__ __forceinline__ int qk_d(int ks, int a) {
+  return KV ? (64 * (ks >> 1) + 16 * a + 8 * (ks & 1)) : (32 * ks + 8 * a);
+}
+
+template <int KV, int D>
+__global__ __launch_bounds__(256, 2) void decode_partial_kernel(const DecodeArgs A) {
+  constexpr int ESZ = KV ? 1 : 2;
+  constexpr int KK = KV ? 2 : 1;      // 32-key PV k-steps per chunk
+  constexpr int CK = 32 * KK;         // keys per chunk
+  constexpr int MT = 2 * KK;          // 16-key S^T m-tiles per chunk
+  constexpr int KS = D / 32;          // QK k-steps
+  constexpr int MD = D / 16;          // O^T m-tiles
+  constexpr int NW = 4;               // waves per workgroup
+  constexpr int KL = KV ? MT * KS / 2 : MT * KS;  // 16-byte K loads per lane per chunk
+
+  __shared__ v4f sh_o[NW - 1][MD][64];
+  __shared__ float sh_m[NW - 1][64];
+  __shared__ float sh_l[NW - 1][64];
+  __shared__ int sh_bad[NW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int a = lane >> 4;
+  const int g = blockIdx.y;
+  const int ct = blockIdx.x % A.col_tiles;
+  const int item = blockIdx.x / A.col_tiles;
+  const int si = find_stream<0>(A.s, A.n_streams, item);
+  const StreamArg& S = A.s[si];
+  const int split = item - S.block_begin;
+  const int G = A.group;
+  if (16 * ct >= G * S.n_rows) return;  // tile holds no column of this stream
+
+  const int col = 16 * ct + n;
+  const int r = col / G;
+  const int hl = col - r * G;
+  const bool col_ok = r < S.n_rows;
+  const int pos = col_ok ? S.first_pos + r : S.n_keys - 1;
+  const int h = g * G + hl;
+
+  v8bf qb[KS];
+  {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(A.q) +
+                        ((int64_t)(S.row_offset + (col_ok ? r : 0)) * A.n_q_heads + h) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      v4u x = load16(qp + qk_d<KV>(ks, a) * 2);
+      if (!col_ok) x = v4u{0, 0, 0, 0};
+      qb[ks] = as_bf(x);
+    }
+  }
+
+  const int k_lo = split * A.split_keys;
+  const int k_hi = min(k_lo + A.split_keys, S.n_keys);
+  const int p_lo = k_lo / kPage;
+  const int p_hi = (k_hi + kPage - 1) / kPage;
+
+  v4f o[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) o[md] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  bool bad = false;
+
+  // S^T row m of m-tile mt holds key 8*KK*(m/4) + 4*mt + m%4 of the chunk.
+  const int krow = 8 * KK * (n >> 2) + (n & 3);
+
+  for (int p = p_lo + wave; p < p_hi; p += NW) {
+    const PageTile T = page_tile<D, ESZ>(S, A.cache, p, g);
+    bad |= !T.ok;
+    const int key_end = min(kPage, k_hi - p * kPage);
+    for (int c0 = 0; c0 < key_end; c0 += CK) {
+      v4u kr[KL], vr[MD];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint8_t* kp = T.k + (int64_t)(c0 + krow + 4 * mt) * D * ESZ;
+        if (KV) {
+#pragma unroll
+          for (int kq = 0; kq < KS / 2; ++kq) kr[mt * (KS / 2) + kq] = load16(kp + 64 * kq + 16 * a);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kr[mt * KS + ks] = load16(kp + (32 * ks + 8 * a) * 2);
+        }
+      }
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+        vr[md] = load16(T.v + ((int64_t)(16 * md + n) * T.v_row + c0 + 8 * KK * a) * ESZ);
+
+      v4f sacc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        sacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          v8bf ka;
+          if (KV) {
+            const v4u x = kr[mt * (KS / 2) + (ks >> 1)];
+            ka = (ks & 1) ? fp8x8_to_bf16(x[2], x[3]) : fp8x8_to_bf16(x[0], x[1]);
+          } else {
+            ka = as_bf(kr[mt * KS + ks]);
+          }
+          sacc[mt] = mfma16(ka, qb[ks], sacc[mt]);
+        }
+      }
+
+      // Online softmax for this lane's column over its 4*MT keys.
+      const int kabs0 = p * kPage + c0 + 8 * KK * a;
+      const bool need_mask = p * kPage + c0 + CK - 1 > S.first_pos;
+      float sv[MT][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = sacc[mt][i] * A.scale_log2;
+          if (need_mask && kabs0 + 4 * mt + i > pos) v = -INFINITY;
+          sv[mt][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[mt][i] = __builtin_amdgcn_exp2f(sv[mt][i] - m_use);
+          psum += sv[mt][i];
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int md = 0; md < MD; ++md) o[md] *= alpha;
+      }
+      v8bf pb[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        v4u x;
+        x[0] = pack_bf2(sv[2 * kk][0], sv[2 * kk][1]);
+        x[1] = pack_bf2(sv[2 * kk][2], sv[2 * kk][3]);
+        x[2] = pack_bf2(sv[2 * kk + 1][0], sv[2 * kk + 1][1]);
+        x[3] = pack_bf2(sv[2 * kk + 1][2], sv[2 * kk + 1][3]);
+        pb[kk] = as_bf(x);
+      }
+
+      // Keys at or past n_keys may be unwritten: their values land as zeros.
+      if (p * kPage + c0 + CK > S.n_keys) {
+        const int nv = S.n_keys - kabs0;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) vr[md] = KV ? keep_first_b(vr[md], nv) : keep_first_h(vr[md], nv);
+      }
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          v8bf va;
+          if (KV)
+            va = kk ? fp8x8_to_bf16(vr[md][2], vr[md][3]) : fp8x8_to_bf16(vr[md][0], vr[md][1]);
+          else
+            va = as_bf(vr[md]);
+          o[md] = mfma16(va, pb[kk], o[md]);
+        }
+    }
+  }
+
+  // Per-column row sum across the four lane groups, in a fixed order.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  if (wave > 0) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md) sh_o[wave - 1][md][lane] = o[md];
+    sh_m[wave - 1][lane] = m_run;
+    sh_l[wave - 1][lane] = l_run;
+  }
+  if (lane == 0) sh_bad[wave] = bad ? 1 : 0;
+  __syncthreads();
+  if (wave != 0) return;
+
+  bool any_bad = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) any_bad |= sh_bad[w] != 0;
+  // Merge waves 1..NW-1 into wave 0 in fixed order.
+  for (int w = 1; w < NW; ++w) {
+    const float mw = sh_m[w - 1][lane];
+    const float lw = sh_l[w - 1][lane];
+    const float M = fmaxf(m_run, mw);
+    if (M == -INFINITY) continue;
+    const float a0 = __builtin_amdgcn_exp2f(m_run - M);
+    const float aw = __builtin_amdgcn_exp2f(mw - M);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) o[md] = o[md] * a0 + sh_o[w - 1][md][lane] * aw;
+    l_run = l_run * a0 + lw * aw;
+    m_run = M;
+  }
+  if (!col_ok) return;
+  const int64_t slot = S.slot_base + ((int64_t)r * A.n_q_heads + h) * S.n_splits + split;
+  if (a == 0) {
+    A.ws_ml[2 * slot] = any_bad ? __builtin_nanf("") : m_run;
+    A.ws_ml[2 * slot + 1] = l_run;
+  }
+  float* dst = A.ws_o + slot * D + 4 * a;
+#pragma unroll
+  for (int md = 0; md < MD; ++md) *reinterpret_cast<v4f*>(dst + 16 * md) = o[md];
+}
+
+// out[row][h] = v_scale * sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j, in
+// split order j = 0, 1, ...; a wholly masked split (m_j = -inf) weighs 0.
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs A) {
+  const int row = blockIdx.x;
+  const int h = blockIdx.y;
+  const int si = find_stream<1>(A.s, A.n_streams, row);
+  const StreamArg& S = A.s[si];
+  const int r = row - S.row_begin;
+  const int ns = S.n_splits;
+  const int64_t slot0 = S.slot_base + ((int64_t)r * A.n_q_heads + h) * ns;
+  const float* ml = A.ws_ml + 2 * slot0;
+  float M = -INFINITY;
+  bool bad = false;
+  for (int j = 0; j < ns; ++j) {
+    const float m = ml[2 * j];
+    bad |= m != m;
+    M = fmaxf(M, m);
+  }
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int j = 0; j < ns; ++j) {
+      const float m = ml[2 * j];
+      const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      num += w * A.ws_o[(slot0 + j) * D + d];
+      den += w * ml[2 * j + 1];
+    }
+    const float res = bad ? __builtin_nanf("") : num / den * A.v_scale;
+    A.out[((int64_t)(S.row_offset + r) * A.n_q_heads + h) * D + d] = f2bf(res);
+  }
+}
+
+template <int KV, int D>
+static int launch_decode_t(const DecodeArgs& A, int n_kv_heads, hipStream_t st) {
+  dim3 g1((unsigned)(A.total_splits * A.col_tiles), (unsigned)n_kv_heads);
+  hipLaunchKernelGGL((decode_partial_kernel<KV, D>), g1, dim3(256), 0, st, A);
+  if (hipGetLastError() != hipSuccess) return -6;
+  dim3 g2((unsigned)A.total_rows, (unsigned)A.n_q_heads);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), g2, dim3(D), 0, st, A);
+  if (hipGetLastError() != hipSuccess) return -6;
+  return 0;
+}
+
+int launch_decode(const DecodeArgs& A, int kv_dtype, int head_dim, int n_kv_heads,
+                  hipStream_t st) {
+  if (kv_dtype == 0 && head_dim == 128) return launch_decode_t<0, 128>(A, n_kv_heads, st);
+  if (kv_dtype == 0 && head_dim == 256) return launch_decode_t<0, 256>(A, n_kv_heads, st);
+  if (kv_dtype == 1 && head_dim == 128) return launch_decode_t<1, 128>(A, n_kv_heads, st);
+  if (kv_dtype == 1 && head_dim == 256) return launch_decode_t<1, 256>(A, n_kv_heads, st);
+  return -7;
+}
+
+}  // namespace pa

@@ -1,0 +1,130 @@
+// Device-side building blocks for the gfx950 kernels: vector types, the MFMA
+// wrapper, exact fp8 -> bf16 conversion, and the page-tile addressing layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_kargs.hpp"
+
+namespace pa {
+
+typedef __bf16 v8bf __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 v2bf __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float v4f __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t v4u __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t v2u __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ v4u load16(const uint8_t* p) {
+  return *reinterpret_cast<const v4u*>(p);
+}
+
+__device__ __forceinline__ v8bf as_bf(v4u x) { return __builtin_bit_cast(v8bf, x); }
+
+// C += A * B for one 16x16x32 bf16 tile.  Per lane: A holds row (lane % 16),
+// k = 8*(lane/16) .. +7; B holds column (lane % 16), the same k run; C holds
+// rows 4*(lane/16) .. +3 of column (lane % 16).
+__device__ __forceinline__ v4f mfma16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight E4M3FN codes (bytes 0..7 of lo:hi) -> eight bf16, exactly (every
+// E4M3FN value is a bf16 value); element order follows byte order.
+__device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  v4u r;
+  r[0] = __builtin_bit_cast(uint32_t, p0);
+  r[1] = __builtin_bit_cast(uint32_t, p1);
+  r[2] = __builtin_bit_cast(uint32_t, p2);
+  r[3] = __builtin_bit_cast(uint32_t, p3);
+  return as_bf(r);
+}
+
+// bf16 (RNE) of a float; gfx950 lowers this to v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint16_t f2bf(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Keep the first `nv` 16-bit elements of an 8 x bf16 vector, zero the rest.
+__device__ __forceinline__ v4u keep_first_h(v4u x, int nv) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t m = (2 * w < nv ? 0x0000FFFFu : 0u) | (2 * w + 1 < nv ? 0xFFFF0000u : 0u);
+    x[w] &= m;
+  }
+  return x;
+}
+
+// Keep the first `nv` bytes of a 16-byte vector, zero the rest.
+__device__ __forceinline__ v4u keep_first_b(v4u x, int nv) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    int k = nv - 4 * w;
+    uint32_t m = k >= 4 ? 0xFFFFFFFFu : (k <= 0 ? 0u : ((1u << (8 * k)) - 1u));
+    x[w] &= m;
+  }
+  return x;
+}
+
+// ----------------------------------------------------------------------------
+// Addressing layer.  A "page tile" is 256 consecutive positions of one kv
+// head: positions 256*t .. 256*t+255 of a stream.  For a paged stream the
+// page id PT[t] is read once per tile (a wave-uniform scalar load) and all
+// key and value addresses inside the tile are base + offset; for a slab the
+// base is computed from the position.  Everything after this call is the
+// same code for both layouts, so paged and slab streams do the same
+// arithmetic on the same bytes.
+//   K: k + (j*D + d)*esz            (j = position - 256*t)
+//   V: v + (d*v_row + j)*esz         (V is dim-major within a tile)
+// `ok` is false when the page id is out of range; the tile then points at
+// page 0 so nothing outside the pool is read, and the caller poisons its
+// result.
+struct PageTile {
+  uint8_t* k;
+  uint8_t* v;
+  int64_t v_row;
+  bool ok;
+};
+
+template <int D, int ESZ>
+__device__ __forceinline__ PageTile page_tile(const StreamArg& s, const CacheArg& c, int t,
+                                              int g) {
+  PageTile r;
+  if (s.layout == 0) {
+    int32_t page = __builtin_amdgcn_readfirstlane(s.page_table[t]);
+    r.ok = (uint32_t)page < (uint32_t)c.n_pages;
+    int64_t base = (int64_t)(r.ok ? page : 0) * c.page_stride;
+    r.k = s.k_base + (base + (int64_t)g * kPage * D) * ESZ;
+    r.v = s.v_base + (base + (int64_t)g * D * kPage) * ESZ;
+    r.v_row = kPage;
+  } else {
+    r.ok = true;
+    r.k = s.k_base + ((int64_t)g * s.slab_cap + (int64_t)t * kPage) * D * ESZ;
+    r.v = s.v_base + ((int64_t)g * D * s.slab_cap + (int64_t)t * kPage) * ESZ;
+    r.v_row = s.slab_cap;
+  }
+  return r;
+}
+
+// Index of the stream that owns launch-local work item `x`: the last stream
+// whose `begin` is <= x (streams with no work are never placed in a launch).
+template <int FIELD>
+__device__ __forceinline__ int find_stream(const StreamArg* s, int n, int x) {
+  int si = 0;
+  for (int i = 1; i < n; ++i) {
+    int b = FIELD == 0 ? s[i].block_begin : s[i].row_begin;
+    if (x >= b) si = i;
+  }
+  return si;
+}
+
+}  // namespace pa

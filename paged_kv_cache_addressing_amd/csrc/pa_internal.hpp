@@ -1,0 +1,16 @@
+// Launchers shared between the kernel translation units and the C ABI layer.
+// Each returns 0, -6 (launch failed) or -7 (no kernel for the shape).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "pa_kargs.hpp"
+
+namespace pa {
+
+int launch_decode(const DecodeArgs& A, int kv_dtype, int head_dim, int n_kv_heads,
+                  hipStream_t st);
+int launch_prefill(const PrefillArgs& A, int kv_dtype, int head_dim, hipStream_t st);
+int launch_write_kv(const WriteArgs& A, int kv_dtype, int head_dim, hipStream_t st);
+
+}  // namespace pa

@@ -1,0 +1,79 @@
+// Kernel-argument blocks shared by the host planner and the gfx950 kernels.
+// Stream descriptors travel by value in the kernarg segment, so a launch
+// stages nothing in device memory and can be captured in a HIP graph.
+#pragma once
+
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kPage = 256;            // positions per page (compile-time everywhere)
+constexpr int kMaxLaunchStreams = 32; // streams per kernel launch; calls are chunked
+constexpr int kPrefillRows = 128;     // query rows per prefill workgroup
+
+struct StreamArg {
+  int32_t layout;       // 0 paged, 1 slab
+  int32_t n_rows;       // query rows of the stream in this call
+  int32_t row_offset;   // first row in q / out / k_new
+  int32_t first_pos;    // absolute position of the first row
+  int32_t n_keys;       // first_pos + n_rows: keys the last row sees
+  int32_t n_splits;     // decode: ceil(n_keys / split_keys)
+  int32_t block_begin;  // decode: first split of the stream in the launch; prefill: first row tile
+  int32_t row_begin;    // first row of the stream in the launch's row numbering
+  int64_t slot_base;    // decode: workspace slot of (row 0, head 0, split 0)
+  const int32_t* page_table;  // paged: device page ids
+  uint8_t* k_base;      // paged: pool K base; slab: slab K base
+  uint8_t* v_base;      // paged: pool V base; slab: slab V base
+  int64_t slab_cap;     // slab: capacity in positions (multiple of 256)
+};
+
+struct CacheArg {
+  int64_t page_stride;  // elements between pages
+  int32_t n_pages;
+  int32_t n_kv_heads;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;    // bf16 [rows][Hq][D]
+  uint16_t* out;        // bf16 [rows][Hq][D]
+  float* ws_o;          // [slots][D] unnormalised partial outputs
+  float* ws_ml;         // [slots][2] (m in log2 units, l)
+  CacheArg cache;
+  int32_t n_q_heads;
+  int32_t group;        // q heads per kv head
+  int32_t split_keys;
+  int32_t n_streams;
+  int32_t total_splits;
+  int32_t col_tiles;    // 16-column MFMA tiles per (split, kv head)
+  int32_t total_rows;   // rows in this launch (merge grid)
+  int32_t pad0;
+  float scale_log2;     // sm_scale * k_scale * log2(e)
+  float v_scale;
+  StreamArg s[kMaxLaunchStreams];
+};
+
+struct PrefillArgs {
+  const uint16_t* q;
+  uint16_t* out;
+  CacheArg cache;
+  int32_t n_q_heads;
+  int32_t group;
+  int32_t n_streams;
+  int32_t total_tiles;  // row tiles in this launch
+  float scale_log2;
+  float v_scale;
+  StreamArg s[kMaxLaunchStreams];
+};
+
+struct WriteArgs {
+  const uint16_t* k_new;  // bf16 [rows][Hkv][D]
+  const uint16_t* v_new;
+  CacheArg cache;
+  int32_t n_streams;
+  int32_t total_rows;
+  float k_scale;
+  float v_scale;
+  StreamArg s[kMaxLaunchStreams];
+};
+
+}  // namespace pa

@@ -1,0 +1,251 @@
+"""GPU parity at small sizes (several tiles, ragged tails, edge cases) and the
+byte-identity rules, through the C ABI.  Expected values come from the
+float64 oracle; byte-identity checks compare the HIP path with itself."""
+from __future__ import annotations
+
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_addressing_amd as pa
+import workloads
+from paged_kv_cache_addressing_amd.resident import upload
+from tests._gpu import decode, launch_error, prefill, references, same_bytes, say, tol
+from tests._util import bits16, oracle_logical, oracle_pool
+
+pytestmark = pytest.mark.gpu
+
+
+def as_slabs(wl):
+    """The same workload with every stream stored in a slab."""
+    w = copy.copy(wl)
+    w.streams = []
+    for st in wl.streams:
+        s = copy.copy(st)
+        s.layout = "slab"
+        s.pages = None
+        s.slab_cap = -(-st.ctx_len // 256) * 256
+        w.streams.append(s)
+    return w
+
+
+def np_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+# ----------------------------------------------------------------------------- write_kv
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_write_kv_bytes_match_oracle_store(dtype, d):
+    wl = workloads.build("store", n_q_heads=4, n_kv_heads=2, head_dim=d, kv_dtype=dtype,
+                         ctx_lens=[700, 300, 513], n_rows=[1, 1, 1],
+                         layouts=["paged", "slab", "paged"], n_pages=8, seed=5)
+    say(f"write_kv {dtype} D={d}")
+    res = upload(wl)
+    kp, vp = oracle_pool(wl)
+    assert np.array_equal(np_bits(res.cache.k_pages), kp)
+    assert np.array_equal(np_bits(res.cache.v_pages), vp.transpose(0, 1, 3, 2))
+    k_log, v_log = oracle_logical(wl, 1)
+    ks, vs = res.slabs[1]
+    assert np.array_equal(np_bits(ks)[:, :300, :], k_log.transpose(1, 0, 2))
+    assert np.array_equal(np_bits(vs)[:, :, :300], v_log.transpose(1, 2, 0))
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0107421875, 3.7])
+def test_fp8_store_every_finite_bf16_value(scale):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_to_f64(bits)
+    fin = bits[np.isfinite(vals)]
+    assert fin.size == 65280
+    rows = torch.from_numpy(fin.view(np.int16).copy()).view(torch.bfloat16).reshape(510, 1, 128)
+    cache = pa.alloc_pool(1, 1, 128, "fp8")
+    cache.k_scale, cache.v_scale = scale, scale * 2
+    ks, vs = pa.alloc_slab(512, 1, 128, "fp8")
+    st = pa.Stream(510, 510, 0, 0, k_slab=ks, v_slab=vs, slab_cap=512, layout=pa.PA_LAYOUT_SLAB)
+    dev = rows.cuda()
+    pa.write_kv(cache, [st], dev, dev)
+    torch.cuda.synchronize()
+    x32 = oracle.bf16_to_f64(fin).astype(np.float32)
+    want_k = oracle.e4m3_encode(x32, scale).reshape(510, 128)
+    want_v = oracle.e4m3_encode(x32, scale * 2).reshape(510, 128)
+    got_k = ks.cpu().numpy()[0, :510, :]
+    got_v = vs.cpu().numpy()[0, :, :510].T
+    bad = np.nonzero(got_k != want_k)
+    assert bad[0].size == 0, (x32.reshape(510, 128)[bad][:8], got_k[bad][:8], want_k[bad][:8])
+    assert np.array_equal(got_v, want_v)
+
+
+# ----------------------------------------------------------------------------- decode
+
+DECODE_CASES = [
+    # name, Hq, Hkv, D, dtype, ctx_lens, rows, layouts, split
+    ("c1", 8, 2, 128, "bf16", [1024], [1], None, 4096),
+    ("ragged-bf16", 24, 4, 256, "bf16", [5000, 300, 4097, 1], [1, 1, 1, 1], None, 4096),
+    ("ragged-fp8-mixed", 24, 4, 256, "fp8", [5000, 9000, 257], [1, 1, 1],
+     ["paged", "slab", "paged"], 4096),
+    ("verify-bf16-d128", 12, 2, 128, "bf16", [2000, 4103], [16, 3], None, 1024),
+    ("verify-fp8-masked-split", 24, 4, 256, "fp8", [4100, 6000, 4096 + 16], [16, 16, 16],
+     None, 4096),
+    ("small-split", 6, 1, 256, "bf16", [3000], [5], None, 256),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_matches_oracle(case):
+    name, hq, hkv, d, dtype, lens, rows, layouts, split = case
+    wl = workloads.build(name, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, kv_dtype=dtype,
+                         ctx_lens=lens, n_rows=rows, layouts=layouts, seed=11,
+                         split_keys=split)
+    say(f"decode {name}")
+    res = upload(wl, poison_tail=True)
+    out = decode(res)
+    refs, sels = references(wl)
+    err = launch_error(wl, out, refs, sels)
+    say(f"decode {name}: normalised error {err:.3e}")
+    assert err <= tol(wl)
+
+
+def test_decode_config1_exact_shape():
+    wl = workloads.config1()
+    res = upload(wl)
+    out = decode(res)
+    refs, sels = references(wl)
+    err = launch_error(wl, out, refs, sels)
+    say(f"decode config1: {err:.3e}")
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_decode_byte_identities(dtype):
+    """paged == slab, alone == beside others, five repeats: all byte-equal."""
+    wl = workloads.build("ident", n_q_heads=24, n_kv_heads=4, head_dim=256, kv_dtype=dtype,
+                         ctx_lens=[9000, 4097, 700], n_rows=[1, 16, 3], seed=21)
+    res = upload(wl)
+    base = decode(res)
+    for _ in range(5):
+        assert same_bytes(decode(res), base)
+    slab = upload(as_slabs(wl))
+    assert same_bytes(decode(slab), base)
+    for i, st in enumerate(res.streams):
+        out = torch.zeros_like(res.q)
+        pa.paged_attn_decode(res.cache, [st], res.q, out=out, sm_scale=res.sm_scale)
+        torch.cuda.synchronize()
+        r0, r1 = st.row_offset, st.row_offset + st.n_rows
+        assert same_bytes(out[r0:r1], base[r0:r1]), f"stream {i} alone differs"
+    # beside a slab stream in the same launch
+    mixed = [res.streams[0], slab.streams[1], res.streams[2]]
+    assert same_bytes(decode(res, streams=mixed), base)
+
+
+def test_decode_swapped_table_control_fails():
+    wl = workloads.build("swap", n_q_heads=8, n_kv_heads=2, head_dim=128, kv_dtype="bf16",
+                         ctx_lens=[1024], n_rows=[1], n_pages=8, seed=1001)
+    res = upload(wl)
+    good = decode(res)
+    refs, sels = references(wl)
+    assert launch_error(wl, good, refs, sels) <= 1e-2
+    pt = res.page_tables[0]
+    bad = pt.clone()
+    bad[1] = int(wl.filler_pages[0])  # an unused pool page instead of the stream's own
+    st = pa.Stream(1024, 1, 0, 1023, page_table=bad)
+    out = decode(res, streams=[st])
+    assert not same_bytes(out, good)
+    assert launch_error(wl, out, refs, sels) > 1e-2
+
+
+def test_decode_poisoned_tail_is_never_read():
+    wl = workloads.build("poison", n_q_heads=24, n_kv_heads=4, head_dim=256, kv_dtype="fp8",
+                         ctx_lens=[1000, 257], n_rows=[1, 2], seed=31)
+    clean = decode(upload(wl))
+    poisoned = decode(upload(wl, poison_tail=True))
+    assert torch.isfinite(poisoned.float()).all()
+    assert same_bytes(clean, poisoned)
+
+
+# ----------------------------------------------------------------------------- prefill
+
+PREFILL_CASES = [
+    # name, Hq, Hkv, D, dtype, ctx_lens, rows, layouts
+    ("rows1", 6, 2, 256, "bf16", [301], [1], None),
+    ("rows127", 6, 2, 256, "bf16", [427], [127], None),
+    ("rows128", 6, 2, 256, "bf16", [428], [128], None),
+    ("rows129", 6, 2, 256, "bf16", [429], [129], None),
+    ("rows257-noprefix", 6, 2, 256, "bf16", [257], [257], None),
+    ("d128", 8, 2, 128, "bf16", [900], [300], None),
+    ("fp8", 6, 2, 256, "fp8", [1000], [300], None),
+    ("two-streams-mixed", 6, 2, 256, "bf16", [700, 1200], [129, 300], ["paged", "slab"]),
+    ("fp8-d128-mixed", 4, 1, 128, "fp8", [513, 2000], [200, 77], ["slab", "paged"]),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_matches_oracle(case):
+    name, hq, hkv, d, dtype, lens, rows, layouts = case
+    wl = workloads.build(name, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, kv_dtype=dtype,
+                         ctx_lens=lens, n_rows=rows, layouts=layouts, seed=41)
+    say(f"prefill {name}")
+    res = upload(wl, poison_tail=True)
+    out = prefill(res)
+    refs, sels = references(wl)
+    err = launch_error(wl, out, refs, sels)
+    say(f"prefill {name}: normalised error {err:.3e}")
+    assert err <= tol(wl)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_prefill_slices_equal_one_launch_and_slab(dtype):
+    wl = workloads.build("slices", n_q_heads=6, n_kv_heads=2, head_dim=256, kv_dtype=dtype,
+                         ctx_lens=[1600], n_rows=[600], seed=51)
+    res = upload(wl)
+    one = prefill(res)
+    st = res.streams[0]
+    for cuts in ([127, 1, 128, 129, 215], [128] * 4 + [88], [257, 256, 87]):
+        out = torch.zeros_like(res.q)
+        off = 0
+        for c in cuts:
+            s = pa.Stream(st.ctx_len, c, off, st.first_pos + off, page_table=st.page_table)
+            pa.paged_attn_prefill(res.cache, [s], res.q, out=out, sm_scale=res.sm_scale)
+            off += c
+        torch.cuda.synchronize()
+        assert off == 600
+        assert same_bytes(out, one), f"slices {cuts} differ from one launch"
+    slab = upload(as_slabs(wl))
+    assert same_bytes(prefill(slab), one)
+    for _ in range(3):
+        assert same_bytes(prefill(res), one)
+
+
+def test_prefill_slices_left_at_row_zero_control_fails():
+    wl = workloads.build("slices0", n_q_heads=6, n_kv_heads=2, head_dim=256, kv_dtype="bf16",
+                         ctx_lens=[800], n_rows=[256], seed=52)
+    res = upload(wl)
+    one = prefill(res)
+    st = res.streams[0]
+    out = torch.zeros_like(res.q)
+    for off in (0, 128):
+        # planted mistake: the second slice keeps the first slice's position
+        s = pa.Stream(st.ctx_len, 128, off, st.first_pos, page_table=st.page_table)
+        pa.paged_attn_prefill(res.cache, [s], res.q, out=out, sm_scale=res.sm_scale)
+    torch.cuda.synchronize()
+    assert not same_bytes(out, one)
+
+
+def test_prefill_stream_alone_equals_beside_others():
+    wl = workloads.build("beside", n_q_heads=6, n_kv_heads=2, head_dim=256, kv_dtype="bf16",
+                         ctx_lens=[700, 1200, 300], n_rows=[129, 300, 5],
+                         layouts=["paged", "slab", "paged"], seed=53)
+    res = upload(wl)
+    both = prefill(res)
+    for st in res.streams:
+        out = torch.zeros_like(res.q)
+        pa.paged_attn_prefill(res.cache, [st], res.q, out=out, sm_scale=res.sm_scale)
+        torch.cuda.synchronize()
+        r0, r1 = st.row_offset, st.row_offset + st.n_rows
+        assert same_bytes(out[r0:r1], both[r0:r1])
