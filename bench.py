@@ -1,0 +1,359 @@
+"""Benchmark: paged decode KV GB/s (and prefill TFLOP/s) on one MI355X.
+
+A step is one decode pass over the batch of 8 streams x 65,536 positions
+(24 q / 4 kv heads, head_dim 256, bf16 KV, 4,096-key splits): write_kv of
+each stream's newest row, the split-K partial kernel, and the merge.
+`value` is KV bytes read per step / step time.  Prefill (4,096 causal rows
+after a 28,672 prefix), the fp8 mixed paged/slab batch and the 16-stream fp8
+verify batch are measured too and reported under "secondary".
+
+Kernel durations come from HIP events recorded on the stream the kernels
+are launched on.  HBM traffic per launch is read from the committed
+rocprofv3 counter summary when it was taken on the current kernel source,
+else reported as null.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-secondary] [--profile decode|prefill|copy|verify]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["paged_kv_cache_addressing_amd/csrc/decode.hip",
+                  "paged_kv_cache_addressing_amd/csrc/prefill.hip",
+                  "paged_kv_cache_addressing_amd/csrc/pa_device.hpp",
+                  "paged_kv_cache_addressing_amd/csrc/pa_kargs.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(paths=KERNEL_SOURCES) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kv_bytes(wl) -> int:
+    """Algorithmic KV bytes a decode pass reads: every visible key's K and V
+    row for every kv head (2 * Hkv * D * element size per position)."""
+    esz = 2 if wl.kv_dtype == "bf16" else 1
+    per_pos = 2 * wl.n_kv_heads * wl.head_dim * esz
+    return sum(st.first_pos + st.n_rows for st in wl.streams) * per_pos
+
+
+def attn_flops(wl) -> int:
+    """4 * D * Hq flop per visible (row, key) pair (QK^T and PV)."""
+    pairs = 0
+    for st in wl.streams:
+        # rows at positions p = first_pos .. first_pos+n_rows-1 see p + 1 keys
+        pairs += st.n_rows * (st.first_pos + 1) + st.n_rows * (st.n_rows - 1) // 2
+    return 4 * wl.head_dim * wl.n_q_heads * pairs
+
+
+class EventTimer:
+    """Accumulates HIP-event durations of work enqueued on the current stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def __enter__(self):
+        import torch
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+        self.s.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.e.record()
+        self.pairs.append((self.s, self.e))
+
+    def mean_ms(self) -> float:
+        import torch
+        torch.cuda.synchronize()
+        ts = [s.elapsed_time(e) for s, e in self.pairs]
+        return sum(ts) / len(ts)
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None if the
+    summary is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("kernel_source_digest") != source_digest():
+        return None
+    ent = t.get("kernels", {}).get(kernel)
+    if not ent or ent.get("workload") != workload:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- decode
+
+def setup_decode(wl):
+    import torch
+
+    import paged_kv_cache_addressing_amd as pa
+    from paged_kv_cache_addressing_amd.resident import upload
+    res = upload(wl)
+    ws = pa.decode_workspace(res.cache, res.streams, wl.n_q_heads, wl.split_keys)
+    out = torch.empty_like(res.q)
+    # the step's store: each stream's newest row (position ctx-1)
+    new_k = torch.stack([wl.k_rows[s][-1] for s in range(len(wl.streams))]).cuda()
+    new_v = torch.stack([wl.v_rows[s][-1] for s in range(len(wl.streams))]).cuda()
+    store = []
+    for s, st in enumerate(res.streams):
+        store.append(pa.Stream(st.ctx_len, 1, s, st.ctx_len - 1, page_table=st.page_table,
+                               k_slab=st.k_slab, v_slab=st.v_slab, slab_cap=st.slab_cap,
+                               layout=st.layout))
+    return res, ws, out, new_k, new_v, store
+
+
+def run_decode(wl, steps, warmup, with_store=True):
+    import torch
+
+    import paged_kv_cache_addressing_amd as pa
+    res, ws, out, nk, nv, store = setup_decode(wl)
+    t_store, t_part, t_merge = EventTimer(), EventTimer(), EventTimer()
+
+    def step(timed):
+        if with_store:
+            if timed:
+                with t_store:
+                    pa.write_kv(res.cache, store, nk, nv)
+            else:
+                pa.write_kv(res.cache, store, nk, nv)
+        if timed:
+            with t_part:
+                pa.paged_attn_decode_partials(res.cache, res.streams, res.q, ws,
+                                              sm_scale=res.sm_scale, split_keys=res.split_keys)
+            with t_merge:
+                pa.paged_attn_decode_merge(res.cache, res.streams, out, ws,
+                                           split_keys=res.split_keys)
+        else:
+            pa.paged_attn_decode(res.cache, res.streams, res.q, out=out, sm_scale=res.sm_scale,
+                                 split_keys=res.split_keys, workspace=ws)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    r = {"ms_per_step": wall_ms, "partial_ms": t_part.mean_ms(), "merge_ms": t_merge.mean_ms()}
+    if with_store:
+        r["store_ms"] = t_store.mean_ms()
+    return r, res, out
+
+
+# ----------------------------------------------------------------------------- prefill
+
+def run_prefill(wl, steps, warmup):
+    import torch
+
+    import paged_kv_cache_addressing_amd as pa
+    from paged_kv_cache_addressing_amd.resident import upload
+    res = upload(wl)
+    out = torch.empty_like(res.q)
+    t = EventTimer()
+    for _ in range(warmup):
+        pa.paged_attn_prefill(res.cache, res.streams, res.q, out=out, sm_scale=res.sm_scale)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        with t:
+            pa.paged_attn_prefill(res.cache, res.streams, res.q, out=out, sm_scale=res.sm_scale)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"ms_per_step": wall_ms, "prefill_ms": t.mean_ms()}
+
+
+# ----------------------------------------------------------------------------- oracle baseline
+
+def cpu_baseline(wl, budget_s: float = 20.0):
+    """Time the float64 oracle on the host over whole streams of the same
+    workload until about budget_s seconds of work; returns KV GB/s."""
+    import numpy as np
+
+    import torch
+
+    import oracle
+
+    def bits16(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    hkv, d = wl.n_kv_heads, wl.head_dim
+    ps = hkv * 256 * d
+    kp = np.zeros((wl.n_pages, hkv, 256, d), np.uint16)
+    vp = np.zeros_like(kp)
+    done_bytes, spent, n_streams = 0, 0.0, 0
+    for s, st in enumerate(wl.streams):
+        oracle.store(kp, vp, oracle.DTYPE_BF16, bits16(wl.k_rows[s]), bits16(wl.v_rows[s]), 0,
+                     page_table=st.pages, page_stride=ps)
+        q = bits16(wl.q[st.row_offset:st.row_offset + st.n_rows])
+        t0 = time.perf_counter()
+        oracle.attention(kp, vp, oracle.DTYPE_BF16, q, st.first_pos, hkv, st.ctx_len,
+                         page_table=st.pages, page_stride=ps, sm_scale=wl.sm_scale,
+                         n_threads=threads)
+        spent += time.perf_counter() - t0
+        done_bytes += (st.first_pos + st.n_rows) * 2 * hkv * d * 2
+        n_streams += 1
+        log(f"oracle: stream {s} done, {spent:.1f}s so far")
+        if spent >= budget_s:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_streams} of {len(wl.streams)} streams of the decode batch, whole "
+                      f"65,536-position context, all 24 q heads, float64 gather+softmax "
+                      f"({spent:.1f} s)"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def copy_calibration():
+    """A plain 1 GiB device copy: reads and writes exactly 2^30 bytes."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--profile", choices=["decode", "prefill", "copy", "verify", "fp8"])
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    torch.cuda.set_device(0)
+
+    if args.profile:  # a short run for rocprofv3: the named kernels only
+        if args.profile == "copy":
+            copy_calibration()
+        elif args.profile == "decode":
+            run_decode(workloads.config2(), args.steps, args.warmup)
+        elif args.profile == "fp8":
+            run_decode(workloads.config3(), args.steps, args.warmup)
+        elif args.profile == "verify":
+            run_decode(workloads.config5(), args.steps, args.warmup, with_store=False)
+        else:
+            run_prefill(workloads.config4(), args.steps, args.warmup)
+        log(f"profile run {args.profile} done")
+        return
+
+    wl = workloads.config2()
+    log(f"decode {wl.name}: uploading")
+    r, res, out = run_decode(wl, args.steps, args.warmup)
+    nbytes = kv_bytes(wl)
+    value = nbytes / (r["ms_per_step"] * 1e-3) / 1e9
+    achieved = nbytes / (r["partial_ms"] * 1e-3) / 1e9
+    log(f"decode: {r}")
+    line = {
+        "metric": "paged decode KV GB/s (% HBM peak); prefill attention TFLOP/s (% MFMA peak)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, shuffled 256-position pages)",
+        "config": {"workload": "decode batch: 8 streams x 1 row at context 65,536, 24 q / 4 kv "
+                               "heads, head_dim 256, bf16 KV in 256-position pages shuffled in "
+                               "one 2,048-page pool, 4,096-key splits + LSE merge",
+                   "streams": 8, "context": 65536, "q_heads": 24, "kv_heads": 4,
+                   "head_dim": 256, "kv_dtype": "bf16", "split_keys": 4096,
+                   "kv_bytes_per_step": nbytes,
+                   "step": "write_kv (1 row/stream) + decode partials + merge"},
+        "roofline": {"bound": "hbm", "kernel": "decode_partial_kernel<bf16,256>",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("decode_partial_kernel<bf16,256>", "config2"),
+                     "kernel_ms": round(r["partial_ms"], 5),
+                     "algorithmic_bytes": nbytes},
+        "kernel_ms": {k: round(v, 5) for k, v in r.items()},
+    }
+    del res, out
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = {}
+        wl4 = workloads.config4()
+        log(f"prefill {wl4.name}")
+        p = run_prefill(wl4, max(3, args.steps // 5), 2)
+        fl = attn_flops(wl4)
+        tf = fl / (p["prefill_ms"] * 1e-3) / 1e12
+        sec["prefill"] = {"workload": "1 stream, 4,096 causal rows after a 28,672-position "
+                                      "paged prefix, 24/4 heads, D 256, bf16",
+                          "kernel": "prefill_kernel<bf16,256>", "kernel_ms": round(p["prefill_ms"], 4),
+                          "flop": fl, "tflops": round(tf, 2), "peak_tflops": BF16_PEAK_TFLOPS,
+                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "bound": "mfma",
+                          "traffic": traffic_for("prefill_kernel<bf16,256>", "config4")}
+        del wl4
+        for name, fn, store in (("decode_fp8_mixed", workloads.config3, True),
+                                ("verify_fp8", workloads.config5, False)):
+            w = fn()
+            log(f"{name} {w.name}")
+            rr, res, out = run_decode(w, args.steps, args.warmup, with_store=store)
+            nb = kv_bytes(w)
+            fl = attn_flops(w)
+            sec[name] = {"workload": w.name, "kv_bytes": nb,
+                         "partial_ms": round(rr["partial_ms"], 5),
+                         "merge_ms": round(rr["merge_ms"], 5),
+                         "kv_gbs_partial": round(nb / (rr["partial_ms"] * 1e-3) / 1e9, 2),
+                         "kv_gbs_step": round(nb / (rr["ms_per_step"] * 1e-3) / 1e9, 2),
+                         "frac_hbm_partial": round(nb / (rr["partial_ms"] * 1e-3) / 1e9 /
+                                                   HBM_PEAK_GBS, 4),
+                         "tflops_partial": round(fl / (rr["partial_ms"] * 1e-3) / 1e12, 2)}
+            del w, res, out
+            torch.cuda.empty_cache()
+        line["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -184,6 +184,30 @@ PA_API int paged_attn_decode(const pa_kv_cache *cache, const pa_stream *streams,
                       int32_t split_keys, void *workspace, size_t workspace_bytes,
                       void *hip_stream);
 
+/* The two halves of paged_attn_decode, for callers that place work
+ * between them (for example partials computed on several devices for one
+ * stream's key shards and gathered into one workspace before the merge).
+ * paged_attn_decode_partials writes every (row, q head, split) triple of the
+ * call into the workspace: o (fp32 [D], unnormalised), m (fp32, log2 units:
+ * the split's largest logit times log2(e)) and l (fp32).  A split wholly
+ * masked for a row stores m = -inf, l = 0, o = 0.  Triple (r, h, j) of the
+ * i-th stream lives at slot  S_i + (r*n_q_heads + h)*n_splits_i + j, where S_i
+ * is the sum of n_rows*n_q_heads*n_splits over earlier streams; o at float
+ * offset slot*head_dim, (m, l) at the second region (byte offset
+ * align256(slots*head_dim*4)) as floats 2*slot and 2*slot+1.
+ * paged_attn_decode_merge reads them back for the same stream descriptors
+ * and split_keys and writes out.  Same validation and errors as
+ * paged_attn_decode. */
+PA_API int paged_attn_decode_partials(const pa_kv_cache *cache, const pa_stream *streams,
+                                      int32_t n_streams, const void *q, int32_t n_q_heads,
+                                      float sm_scale, int32_t split_keys, void *workspace,
+                                      size_t workspace_bytes, void *hip_stream);
+
+PA_API int paged_attn_decode_merge(const pa_kv_cache *cache, const pa_stream *streams,
+                                   int32_t n_streams, void *out, int32_t n_q_heads,
+                                   int32_t split_keys, const void *workspace,
+                                   size_t workspace_bytes, void *hip_stream);
+
 /* Launch plan of a decode call, for callers that size grids or check
  * scheduling: per stream its split count (splits_out, n_streams entries, may
  * be NULL), and the totals.  Host only; validates like paged_attn_decode

@@ -32,8 +32,8 @@ PA_LAYOUT_PAGED, PA_LAYOUT_SLAB = 0, 1
 
 EXPORTS = ["pa_status_string", "pa_version", "page_pool_create", "page_pool_destroy",
            "page_pool_alloc", "page_pool_free", "page_pool_free_count", "write_kv",
-           "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_plan",
-           "paged_attn_prefill"]
+           "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_partials",
+           "paged_attn_decode_merge", "paged_attn_decode_plan", "paged_attn_prefill"]
 
 
 class PagedAttnError(RuntimeError):
@@ -95,6 +95,12 @@ def lib():
         L.paged_attn_decode.restype = C.c_int
         L.paged_attn_decode.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream), i32, P, P,
                                         i32, f32, i32, P, sz, P]
+        L.paged_attn_decode_partials.restype = C.c_int
+        L.paged_attn_decode_partials.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream),
+                                                 i32, P, i32, f32, i32, P, sz, P]
+        L.paged_attn_decode_merge.restype = C.c_int
+        L.paged_attn_decode_merge.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream), i32,
+                                              P, i32, i32, P, sz, P]
         L.paged_attn_decode_plan.restype = C.c_int
         L.paged_attn_decode_plan.argtypes = [C.POINTER(pa_stream), i32, i32, i32, i32, i32, P,
                                              C.POINTER(pa_decode_plan)]
@@ -306,6 +312,40 @@ def paged_attn_decode(cache: KVCache, streams, q, out=None, sm_scale: float | No
                                    float(sm_scale), int(split_keys), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(),
                                    _hip_stream(stream)), "paged_attn_decode")
+    return out
+
+
+def decode_workspace(cache: KVCache, streams, n_q_heads: int,
+                     split_keys: int = DEFAULT_SPLIT_KEYS, device="cuda"):
+    """A device workspace tensor large enough for a decode call."""
+    import torch
+    nb = paged_attn_decode_workspace_size(streams, n_q_heads, cache.head_dim, split_keys)
+    return torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
+
+
+def paged_attn_decode_partials(cache: KVCache, streams, q, workspace,
+                               sm_scale: float | None = None,
+                               split_keys: int = DEFAULT_SPLIT_KEYS, stream=None) -> None:
+    """Split partials (m, l, o) of every (row, head, split) into workspace."""
+    if sm_scale is None:
+        sm_scale = cache.head_dim ** -0.5
+    arr, n = _streams(streams)
+    cc = cache.c()
+    _check(lib().paged_attn_decode_partials(C.byref(cc), arr, n, _ptr(q), int(q.shape[1]),
+                                            float(sm_scale), int(split_keys), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(),
+                                            _hip_stream(stream)), "paged_attn_decode_partials")
+
+
+def paged_attn_decode_merge(cache: KVCache, streams, out, workspace,
+                            split_keys: int = DEFAULT_SPLIT_KEYS, stream=None):
+    """Fixed-order LSE merge of the workspace partials into out (bf16)."""
+    arr, n = _streams(streams)
+    cc = cache.c()
+    _check(lib().paged_attn_decode_merge(C.byref(cc), arr, n, _ptr(out), int(out.shape[1]),
+                                         int(split_keys), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(),
+                                         _hip_stream(stream)), "paged_attn_decode_merge")
     return out
 
 

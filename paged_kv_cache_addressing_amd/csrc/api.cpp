@@ -305,18 +305,25 @@ int paged_attn_decode_plan(const pa_stream* streams, int32_t n_streams, int32_t 
   return PA_OK;
 }
 
-int paged_attn_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n_streams,
-                      const void* q, void* out, int32_t n_q_heads, float sm_scale,
-                      int32_t split_keys, void* workspace, size_t workspace_bytes,
-                      void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Validate a decode call and build one kernel-argument block per launch
+// group.  `need_q` / `need_out` say which of q and out the caller uses.
+int prepare_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n_streams,
+                   const void* q, void* out, int32_t n_q_heads, float sm_scale,
+                   int32_t split_keys, void* workspace, size_t workspace_bytes, bool need_q,
+                   bool need_out, std::vector<pa::DecodeArgs>& launches) {
+  launches.clear();
   int rc = check_call(cache, streams, n_streams, n_q_heads, PA_DECODE_MAX_ROWS);
   if (rc != PA_OK) return rc;
-  if (!(std::isfinite(sm_scale) && sm_scale > 0.f)) return PA_EINVAL;
+  if (need_q && !(std::isfinite(sm_scale) && sm_scale > 0.f)) return PA_EINVAL;
   DecodePlan P;
   rc = plan_decode(streams, n_streams, n_q_heads, split_keys, P);
   if (rc != PA_OK) return rc;
   if (P.groups.empty()) return PA_OK;
-  if (!q || !out) return PA_EINVAL;
+  if ((need_q && !q) || (need_out && !out)) return PA_EINVAL;
   const size_t need = ws_bytes(P.total_slots, cache->head_dim);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return PA_EWORKSPACE;
   float* ws_o = static_cast<float*>(workspace);
@@ -352,8 +359,58 @@ int paged_attn_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_
     }
     A.total_splits = splits;
     A.total_rows = rows;
-    rc = pa::launch_decode(A, cache->dtype, cache->head_dim, cache->n_kv_heads,
-                           (hipStream_t)hip_stream);
+    launches.push_back(A);
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode_partials(const pa_kv_cache* cache, const pa_stream* streams,
+                               int32_t n_streams, const void* q, int32_t n_q_heads,
+                               float sm_scale, int32_t split_keys, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
+  std::vector<pa::DecodeArgs> L;
+  int rc = prepare_decode(cache, streams, n_streams, q, nullptr, n_q_heads, sm_scale,
+                          split_keys, workspace, workspace_bytes, true, false, L);
+  if (rc != PA_OK) return rc;
+  for (const auto& A : L) {
+    rc = pa::launch_decode_partials(A, cache->dtype, cache->head_dim, cache->n_kv_heads,
+                                    (hipStream_t)hip_stream);
+    if (rc != 0) return rc;
+  }
+  return PA_OK;
+}
+
+int paged_attn_decode_merge(const pa_kv_cache* cache, const pa_stream* streams,
+                            int32_t n_streams, void* out, int32_t n_q_heads, int32_t split_keys,
+                            const void* workspace, size_t workspace_bytes, void* hip_stream) {
+  std::vector<pa::DecodeArgs> L;
+  int rc = prepare_decode(cache, streams, n_streams, nullptr, out, n_q_heads, 1.f, split_keys,
+                          const_cast<void*>(workspace), workspace_bytes, false, true, L);
+  if (rc != PA_OK) return rc;
+  for (const auto& A : L) {
+    rc = pa::launch_decode_merge(A, cache->head_dim, (hipStream_t)hip_stream);
+    if (rc != 0) return rc;
+  }
+  return PA_OK;
+}
+
+int paged_attn_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n_streams,
+                      const void* q, void* out, int32_t n_q_heads, float sm_scale,
+                      int32_t split_keys, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  std::vector<pa::DecodeArgs> L;
+  int rc = prepare_decode(cache, streams, n_streams, q, out, n_q_heads, sm_scale, split_keys,
+                          workspace, workspace_bytes, true, true, L);
+  if (rc != PA_OK) return rc;
+  for (const auto& A : L) {
+    rc = pa::launch_decode_partials(A, cache->dtype, cache->head_dim, cache->n_kv_heads,
+                                    (hipStream_t)hip_stream);
+    if (rc != 0) return rc;
+    rc = pa::launch_decode_merge(A, cache->head_dim, (hipStream_t)hip_stream);
     if (rc != 0) return rc;
   }
   return PA_OK;

@@ -269,23 +269,30 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs A) {
 }
 
 template <int KV, int D>
-static int launch_decode_t(const DecodeArgs& A, int n_kv_heads, hipStream_t st) {
-  dim3 g1((unsigned)(A.total_splits * A.col_tiles), (unsigned)n_kv_heads);
-  hipLaunchKernelGGL((decode_partial_kernel<KV, D>), g1, dim3(256), 0, st, A);
-  if (hipGetLastError() != hipSuccess) return -6;
-  dim3 g2((unsigned)A.total_rows, (unsigned)A.n_q_heads);
-  hipLaunchKernelGGL((decode_merge_kernel<D>), g2, dim3(D), 0, st, A);
-  if (hipGetLastError() != hipSuccess) return -6;
-  return 0;
+static int launch_partials_t(const DecodeArgs& A, int n_kv_heads, hipStream_t st) {
+  dim3 grid((unsigned)(A.total_splits * A.col_tiles), (unsigned)n_kv_heads);
+  hipLaunchKernelGGL((decode_partial_kernel<KV, D>), grid, dim3(256), 0, st, A);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-int launch_decode(const DecodeArgs& A, int kv_dtype, int head_dim, int n_kv_heads,
-                  hipStream_t st) {
-  if (kv_dtype == 0 && head_dim == 128) return launch_decode_t<0, 128>(A, n_kv_heads, st);
-  if (kv_dtype == 0 && head_dim == 256) return launch_decode_t<0, 256>(A, n_kv_heads, st);
-  if (kv_dtype == 1 && head_dim == 128) return launch_decode_t<1, 128>(A, n_kv_heads, st);
-  if (kv_dtype == 1 && head_dim == 256) return launch_decode_t<1, 256>(A, n_kv_heads, st);
+int launch_decode_partials(const DecodeArgs& A, int kv_dtype, int head_dim, int n_kv_heads,
+                           hipStream_t st) {
+  if (kv_dtype == 0 && head_dim == 128) return launch_partials_t<0, 128>(A, n_kv_heads, st);
+  if (kv_dtype == 0 && head_dim == 256) return launch_partials_t<0, 256>(A, n_kv_heads, st);
+  if (kv_dtype == 1 && head_dim == 128) return launch_partials_t<1, 128>(A, n_kv_heads, st);
+  if (kv_dtype == 1 && head_dim == 256) return launch_partials_t<1, 256>(A, n_kv_heads, st);
   return -7;
+}
+
+int launch_decode_merge(const DecodeArgs& A, int head_dim, hipStream_t st) {
+  dim3 grid((unsigned)A.total_rows, (unsigned)A.n_q_heads);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(128), 0, st, A);
+  else if (head_dim == 256)
+    hipLaunchKernelGGL((decode_merge_kernel<256>), grid, dim3(256), 0, st, A);
+  else
+    return -7;
+  return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
 }  // namespace pa
