@@ -84,12 +84,16 @@ typedef enum pa_layout {
  * block inside a multi-layer pool when page_stride is larger).
  *
  * K, page p, kv head g, slot j (position 256*t + j of the page's stream),
- * dim d: element  p*page_stride + (g*256 + j)*head_dim + d        (head-major)
- * V, same:       element  p*page_stride + (g*head_dim + d)*256 + j (transposed)
+ * dim d: element  p*page_stride + (g*256 + j)*head_dim + d            (head-major)
+ * V, same: element  p*page_stride + g*256*head_dim
+ *                   + ((j/VB)*head_dim + d)*VB + j%VB               (key blocks)
+ * with VB = 64 / element size (32 keys for bf16, 64 for fp8): V is kept in
+ * 64-byte key blocks, dim-major inside a block.
  *
- * Elements are bf16 (2 bytes) or E4M3FN codes (1 byte) per `dtype`.  V is
- * stored dim-major inside a page so that the MFMA operand of P.V (eight
- * consecutive keys of one dim) is one contiguous 16-byte load.
+ * Elements are bf16 (2 bytes) or E4M3FN codes (1 byte) per `dtype`.  The V
+ * layout makes the MFMA operand of P.V (eight consecutive keys of one dim)
+ * one 16-byte load, and makes a chunk of VB keys one contiguous run of
+ * head_dim*64 bytes, so every HBM line a chunk reads is used whole.
  */
 typedef struct pa_kv_cache {
   void *k_pages;         /* device, may be NULL if no stream is paged */
@@ -104,9 +108,10 @@ typedef struct pa_kv_cache {
 } pa_kv_cache;
 
 /*
- * One stream (sequence) of a launch.  Slab layout, capacity C positions:
- * K element (g*C + t)*head_dim + d, V element (g*head_dim + d)*C + t, same
- * dtype as the cache.  C must be a multiple of 256.
+ * One stream (sequence) of a launch.  Slab layout, capacity C positions (a
+ * multiple of 256), same dtype as the cache: K element (g*C + t)*head_dim + d;
+ * V element g*C*head_dim + ((t/VB)*head_dim + d)*VB + t%VB (the page layout
+ * of V repeated over the slab).
  */
 typedef struct pa_stream {
   int32_t layout;          /* pa_layout */
@@ -188,7 +193,8 @@ PA_API int paged_attn_decode(const pa_kv_cache *cache, const pa_stream *streams,
  * between them (for example partials computed on several devices for one
  * stream's key shards and gathered into one workspace before the merge).
  * paged_attn_decode_partials writes every (row, q head, split) triple of the
- * call into the workspace: o (fp32 [D], unnormalised), m (fp32, log2 units:
+ * call into the workspace: o (fp32 [D], unnormalised, in units of the stored
+ * V values: the merge applies v_scale for fp8), m (fp32, log2 units:
  * the split's largest logit times log2(e)) and l (fp32).  A split wholly
  * masked for a row stores m = -inf, l = 0, o = 0.  Triple (r, h, j) of the
  * i-th stream lives at slot  S_i + (r*n_q_heads + h)*n_splits_i + j, where S_i

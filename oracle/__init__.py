@@ -52,7 +52,7 @@ def _load():
         lib.oracle_e4m3_to_f64_array.restype = None
         lib.oracle_e4m3_to_f64_array.argtypes = [P, i64, P]
         lib.oracle_store.restype = i32
-        lib.oracle_store.argtypes = [P, P, i32, f32, f32, P, i64, i32, i32, P, P, i64, i64]
+        lib.oracle_store.argtypes = [P, P, i32, f32, f32, P, i64, i32, i32, P, P, i64, i64, i32]
         lib.oracle_gather.restype = i32
         lib.oracle_gather.argtypes = [P, P, i32, f64, f64, P, i64, i32, i32, i64, P, P]
         lib.oracle_attention.restype = i32
@@ -105,7 +105,8 @@ def e4m3_encode(x: np.ndarray, scale: float) -> np.ndarray:
 
 def store(k_dst: np.ndarray, v_dst: np.ndarray, dtype: int, k_rows: np.ndarray,
           v_rows: np.ndarray, first_pos: int, page_table: np.ndarray | None = None,
-          page_stride: int = 0, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+          page_stride: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
+          n_threads: int = 0) -> None:
     """Write rows ``[n][Hkv][D]`` (bf16 bits) at positions first_pos.. into the
     oracle-layout cache arrays ``k_dst``/``v_dst`` (modified in place)."""
     n, hkv, d = k_rows.shape
@@ -114,7 +115,7 @@ def store(k_dst: np.ndarray, v_dst: np.ndarray, dtype: int, k_rows: np.ndarray,
     assert k_dst.flags.c_contiguous and v_dst.flags.c_contiguous
     rc = _load().oracle_store(_ptr(k_dst), _ptr(v_dst), dtype, float(k_scale), float(v_scale),
                               _ptr(pt), int(page_stride), hkv, d, _ptr(kr), _ptr(vr),
-                              int(first_pos), n)
+                              int(first_pos), n, int(n_threads))
     if rc != 0:
         raise ValueError(f"oracle_store failed ({rc})")
 

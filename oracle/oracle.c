@@ -141,31 +141,77 @@ static double oracle_decode(const void *base, int dtype, int64_t idx, double sca
 }
 
 /* Write n_rows new rows (bf16 bits, [n_rows][Hkv][D]) at positions
- * first_pos.. into the cache, quantising for fp8.  Returns 0, or -1 on a bad
- * argument. */
-int oracle_store(void *k_dst, void *v_dst, int dtype, float k_scale, float v_scale,
-                 const int32_t *page_table, int64_t page_stride, int n_kv_heads, int head_dim,
-                 const uint16_t *k_rows, const uint16_t *v_rows, int64_t first_pos,
-                 int64_t n_rows) {
-  if (dtype != ORACLE_DTYPE_BF16 && dtype != ORACLE_DTYPE_E4M3) return -1;
-  for (int64_t i = 0; i < n_rows; ++i) {
-    int64_t t = first_pos + i;
-    for (int g = 0; g < n_kv_heads; ++g) {
-      int64_t dst = oracle_offset(page_table, page_stride, n_kv_heads, head_dim, t, g);
-      int64_t src = (i * n_kv_heads + g) * (int64_t)head_dim;
-      for (int d = 0; d < head_dim; ++d) {
-        if (dtype == ORACLE_DTYPE_BF16) {
-          ((uint16_t *)k_dst)[dst + d] = k_rows[src + d];
-          ((uint16_t *)v_dst)[dst + d] = v_rows[src + d];
+ * first_pos.. into the cache, quantising for fp8.  Rows are independent, so
+ * they are shared out over n_threads threads (0: one per online core).
+ * Returns 0, or -1 on a bad argument. */
+typedef struct {
+  void *k_dst, *v_dst;
+  int dtype;
+  float k_scale, v_scale;
+  const int32_t *page_table;
+  int64_t page_stride;
+  int n_kv_heads, head_dim;
+  const uint16_t *k_rows, *v_rows;
+  int64_t first_pos, lo, hi;
+} oracle_store_job;
+
+static void *oracle_store_rows(void *arg) {
+  oracle_store_job *J = (oracle_store_job *)arg;
+  for (int64_t i = J->lo; i < J->hi; ++i) {
+    int64_t t = J->first_pos + i;
+    for (int g = 0; g < J->n_kv_heads; ++g) {
+      int64_t dst = oracle_offset(J->page_table, J->page_stride, J->n_kv_heads, J->head_dim, t, g);
+      int64_t src = (i * J->n_kv_heads + g) * (int64_t)J->head_dim;
+      for (int d = 0; d < J->head_dim; ++d) {
+        if (J->dtype == ORACLE_DTYPE_BF16) {
+          ((uint16_t *)J->k_dst)[dst + d] = J->k_rows[src + d];
+          ((uint16_t *)J->v_dst)[dst + d] = J->v_rows[src + d];
         } else {
-          float kx = (float)oracle_bf16_to_f64(k_rows[src + d]);
-          float vx = (float)oracle_bf16_to_f64(v_rows[src + d]);
-          ((uint8_t *)k_dst)[dst + d] = oracle_e4m3_encode(kx, k_scale);
-          ((uint8_t *)v_dst)[dst + d] = oracle_e4m3_encode(vx, v_scale);
+          float kx = (float)oracle_bf16_to_f64(J->k_rows[src + d]);
+          float vx = (float)oracle_bf16_to_f64(J->v_rows[src + d]);
+          ((uint8_t *)J->k_dst)[dst + d] = oracle_e4m3_encode(kx, J->k_scale);
+          ((uint8_t *)J->v_dst)[dst + d] = oracle_e4m3_encode(vx, J->v_scale);
         }
       }
     }
   }
+  return NULL;
+}
+
+int oracle_store(void *k_dst, void *v_dst, int dtype, float k_scale, float v_scale,
+                 const int32_t *page_table, int64_t page_stride, int n_kv_heads, int head_dim,
+                 const uint16_t *k_rows, const uint16_t *v_rows, int64_t first_pos,
+                 int64_t n_rows, int n_threads) {
+  oracle_store_job jobs[256];
+  pthread_t th[256];
+  int started[256];
+  int i;
+  if (dtype != ORACLE_DTYPE_BF16 && dtype != ORACLE_DTYPE_E4M3) return -1;
+  if (n_threads <= 0) n_threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 256) n_threads = 256;
+  if (n_rows < 4096) n_threads = 1;
+  for (i = 0; i < n_threads; ++i) {
+    oracle_store_job *J = &jobs[i];
+    J->k_dst = k_dst;
+    J->v_dst = v_dst;
+    J->dtype = dtype;
+    J->k_scale = k_scale;
+    J->v_scale = v_scale;
+    J->page_table = page_table;
+    J->page_stride = page_stride;
+    J->n_kv_heads = n_kv_heads;
+    J->head_dim = head_dim;
+    J->k_rows = k_rows;
+    J->v_rows = v_rows;
+    J->first_pos = first_pos;
+    J->lo = n_rows * i / n_threads;
+    J->hi = n_rows * (i + 1) / n_threads;
+    started[i] = pthread_create(&th[i], NULL, oracle_store_rows, J) == 0;
+    if (!started[i]) oracle_store_rows(J);
+  }
+  for (i = 0; i < n_threads; ++i)
+    if (started[i]) pthread_join(th[i], NULL);
   return 0;
 }
 

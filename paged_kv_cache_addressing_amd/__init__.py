@@ -139,7 +139,8 @@ def _hip_stream(stream):
 class KVCache:
     """Device pool tensors plus geometry; see pa_kv_cache in paged_attn.h.
 
-    K page layout [n_pages][Hkv][256][D]; V page layout [n_pages][Hkv][D][256].
+    K page layout [n_pages][Hkv][256][D]; V page layout
+    [n_pages][Hkv][256/VB][D][VB] with VB = 64 bytes of keys (see v_block).
     dtype: "bf16" (torch.bfloat16 storage) or "fp8" (uint8 E4M3FN codes).
     """
     k_pages: object
@@ -169,7 +170,7 @@ class Stream:
     first_pos: int
     page_table: object = None     # torch.int32 device tensor (paged)
     k_slab: object = None         # device tensor [Hkv][cap][D]
-    v_slab: object = None         # device tensor [Hkv][D][cap]
+    v_slab: object = None         # device tensor [Hkv][cap/VB][D][VB]
     slab_cap: int = 0
     layout: int = PA_LAYOUT_PAGED
 
@@ -186,25 +187,35 @@ def _streams(streams):
     return arr, len(streams)
 
 
+def v_block(dtype: str) -> int:
+    """Keys per V block (64 bytes of one dim): 32 for bf16, 64 for fp8."""
+    return 32 if dtype == "bf16" else 64
+
+
 def alloc_pool(n_pages: int, n_kv_heads: int, head_dim: int, dtype: str = "bf16",
                device="cuda", zero: bool = True) -> KVCache:
-    """Allocate pool tensors on the device (torch memory, caller-owned)."""
+    """Allocate pool tensors on the device (torch memory, caller-owned).
+
+    K: [n_pages][Hkv][256][D]; V: [n_pages][Hkv][256/VB][D][VB] (see v_block).
+    """
     import torch
     tdt = torch.bfloat16 if dtype == "bf16" else torch.uint8
+    vb = v_block(dtype)
     mk = torch.zeros if zero else torch.empty
     k = mk((n_pages, n_kv_heads, PAGE_POSITIONS, head_dim), dtype=tdt, device=device)
-    v = mk((n_pages, n_kv_heads, head_dim, PAGE_POSITIONS), dtype=tdt, device=device)
+    v = mk((n_pages, n_kv_heads, PAGE_POSITIONS // vb, head_dim, vb), dtype=tdt, device=device)
     return KVCache(k, v, n_pages, n_kv_heads, head_dim, dtype)
 
 
 def alloc_slab(cap: int, n_kv_heads: int, head_dim: int, dtype: str = "bf16", device="cuda",
                zero: bool = True):
-    """Slab tensors K [Hkv][cap][D] and V [Hkv][D][cap]; cap a multiple of 256."""
+    """Slab tensors K [Hkv][cap][D] and V [Hkv][cap/VB][D][VB]; cap a multiple of 256."""
     import torch
     tdt = torch.bfloat16 if dtype == "bf16" else torch.uint8
+    vb = v_block(dtype)
     mk = torch.zeros if zero else torch.empty
     return (mk((n_kv_heads, cap, head_dim), dtype=tdt, device=device),
-            mk((n_kv_heads, head_dim, cap), dtype=tdt, device=device))
+            mk((n_kv_heads, cap // vb, head_dim, vb), dtype=tdt, device=device))
 
 
 # ----------------------------------------------------------------------------- page pool

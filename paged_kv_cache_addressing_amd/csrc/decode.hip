@@ -10,8 +10,9 @@
 // MFMA mapping (v_mfma_f32_16x16x32_bf16, wave64):
 //   S^T = K Q^T : A = 16 keys x 32 dims of K, B = 32 dims x 16 columns of Q^T,
 //                 a column being one (query row, q head of the group).
-//   O^T += V^T P^T : A = 16 dims x 32 keys of V^T (V is dim-major inside a
-//                 page, so a lane's 8 keys are one 16-byte load), B = P^T.
+//   O^T += V^T P^T : A = 16 dims x 32 keys of V^T (V is dim-major inside
+//                 64-byte key blocks, so a lane's 8 keys are one 16-byte
+//                 load and a chunk's V is one contiguous run), B = P^T.
 // The keys of each S^T m-tile are permuted so that the C-layout rows a lane
 // ends up holding are exactly the 8 consecutive keys its P^T operand needs:
 // no data moves between the two products.  K and V go straight from HBM to
@@ -110,9 +111,10 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(const DecodeArgs
           for (int ks = 0; ks < KS; ++ks) kr[mt * KS + ks] = load16(kp + (32 * ks + 8 * a) * 2);
         }
       }
+      // V block of this chunk (CK == 64/ESZ keys): D rows of 64 bytes.
+      const uint8_t* vb = T.v + (int64_t)c0 * D * ESZ + (8 * KK * a) * ESZ;
 #pragma unroll
-      for (int md = 0; md < MD; ++md)
-        vr[md] = load16(T.v + ((int64_t)(16 * md + n) * T.v_row + c0 + 8 * KK * a) * ESZ);
+      for (int md = 0; md < MD; ++md) vr[md] = load16(vb + (16 * md + n) * 64);
 
       v4f sacc[MT];
 #pragma unroll

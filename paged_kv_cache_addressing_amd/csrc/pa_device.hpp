@@ -82,18 +82,32 @@ __device__ __forceinline__ v4u keep_first_b(v4u x, int nv) {
 // key and value addresses inside the tile are base + offset; for a slab the
 // base is computed from the position.  Everything after this call is the
 // same code for both layouts, so paged and slab streams do the same
-// arithmetic on the same bytes.
-//   K: k + (j*D + d)*esz            (j = position - 256*t)
-//   V: v + (d*v_row + j)*esz         (V is dim-major within a tile)
+// arithmetic on the same bytes.  Inside a tile (j = position - 256*t):
+//   K(j, d): k + (j*D + d)*esz                          (key-major rows)
+//   V(j, d): v + (((j/VB)*D + d)*VB + j%VB)*esz          (VB = 64/esz keys)
+// V is kept in blocks of VB keys, dim-major inside a block: the P.V operand
+// (8 consecutive keys of one dim) is one 16-byte load, and the V operand of
+// a VB-key chunk is one contiguous run of D*64 bytes, so every HBM line a
+// chunk touches is used whole.
 // `ok` is false when the page id is out of range; the tile then points at
 // page 0 so nothing outside the pool is read, and the caller poisons its
 // result.
 struct PageTile {
   uint8_t* k;
   uint8_t* v;
-  int64_t v_row;
   bool ok;
 };
+
+// Keys per V block: 64 bytes of one dim.
+template <int ESZ>
+constexpr int v_block() { return 64 / ESZ; }
+
+// Element offset of V(j, d) inside a tile.
+template <int D, int ESZ>
+__device__ __forceinline__ int v_off(int j, int d) {
+  constexpr int VB = v_block<ESZ>();
+  return ((j / VB) * D + d) * VB + (j % VB);
+}
 
 template <int D, int ESZ>
 __device__ __forceinline__ PageTile page_tile(const StreamArg& s, const CacheArg& c, int t,
@@ -102,15 +116,14 @@ __device__ __forceinline__ PageTile page_tile(const StreamArg& s, const CacheArg
   if (s.layout == 0) {
     int32_t page = __builtin_amdgcn_readfirstlane(s.page_table[t]);
     r.ok = (uint32_t)page < (uint32_t)c.n_pages;
-    int64_t base = (int64_t)(r.ok ? page : 0) * c.page_stride;
-    r.k = s.k_base + (base + (int64_t)g * kPage * D) * ESZ;
-    r.v = s.v_base + (base + (int64_t)g * D * kPage) * ESZ;
-    r.v_row = kPage;
+    int64_t base = (int64_t)(r.ok ? page : 0) * c.page_stride + (int64_t)g * kPage * D;
+    r.k = s.k_base + base * ESZ;
+    r.v = s.v_base + base * ESZ;
   } else {
     r.ok = true;
-    r.k = s.k_base + ((int64_t)g * s.slab_cap + (int64_t)t * kPage) * D * ESZ;
-    r.v = s.v_base + ((int64_t)g * D * s.slab_cap + (int64_t)t * kPage) * ESZ;
-    r.v_row = s.slab_cap;
+    int64_t base = ((int64_t)g * s.slab_cap + (int64_t)t * kPage) * D;
+    r.k = s.k_base + base * ESZ;
+    r.v = s.v_base + base * ESZ;
   }
   return r;
 }

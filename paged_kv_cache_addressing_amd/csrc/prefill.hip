@@ -118,12 +118,12 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       if (KV) {
         const int md = q >> 6;
         const int d = 16 * md + (lp & 15);
-        st_v[i] = load16(T.v + (int64_t)d * T.v_row + o + 16 * (lp >> 4));
+        st_v[i] = load16(T.v + v_off<D, ESZ>(o + 16 * (lp >> 4), d));
       } else {
         const int f = q >> 6;
         const int md = f >> 1, kk = f & 1;
         const int d = 16 * md + (lp & 15);
-        st_v[i] = load16(T.v + ((int64_t)d * T.v_row + o + 16 * (lp >> 4) + 8 * kk) * 2);
+        st_v[i] = load16(T.v + v_off<D, ESZ>(o + 16 * (lp >> 4) + 8 * kk, d) * 2);
       }
     }
   };

@@ -2,7 +2,7 @@
 // quantising to E4M3FN for fp8 caches.  The layout written is the one every
 // attention kernel reads (TensorFold pull request #1373, "What changes": the
 // tiles read the layout the stores write): K head-major [g][slot][D] and V
-// dim-major [g][D][slot] inside each 256-position page.
+// in 64-byte key blocks, dim-major inside a block, [g][slot/VB][D][slot%VB].
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const WriteArgs A) {
     const uint16_t kx = A.k_new[src + d];
     const uint16_t vx = A.v_new[src + d];
     uint8_t* kd = T.k + ((int64_t)j * D + d) * ESZ;
-    uint8_t* vd = T.v + ((int64_t)d * T.v_row + j) * ESZ;
+    uint8_t* vd = T.v + (int64_t)v_off<D, ESZ>(j, d) * ESZ;
     if (KV) {
       *kd = (uint8_t)enc_e4m3(bf2f(kx), A.k_scale);
       *vd = (uint8_t)enc_e4m3(bf2f(vx), A.v_scale);

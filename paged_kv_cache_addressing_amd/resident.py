@@ -62,8 +62,13 @@ def upload(wl, device: str = "cuda", poison_tail: bool = False,
                     nan = torch.tensor(0x7FC0, dtype=torch.int16).view(torch.bfloat16)
                 else:
                     nan = torch.tensor(0x7F, dtype=torch.uint8)
-                cache.k_pages[last, :, j0:, :] = nan.to(device)
-                cache.v_pages[last, :, :, j0:] = nan.to(device)
+                nan = nan.to(device)
+                cache.k_pages[last, :, j0:, :] = nan
+                vb = cache.v_pages.shape[-1]
+                for b in range(PAGE_POSITIONS // vb):
+                    start = max(j0 - b * vb, 0)
+                    if start < vb:
+                        cache.v_pages[last, :, b, :, start:] = nan
             desc = Stream(st.ctx_len, st.ctx_len, at, 0, page_table=pt, layout=PA_LAYOUT_PAGED)
             att = Stream(st.ctx_len, st.n_rows, st.row_offset, st.first_pos, page_table=pt,
                          layout=PA_LAYOUT_PAGED)

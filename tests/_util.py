@@ -68,3 +68,11 @@ def oracle_reference(wl, s, rows=None, pool=None, n_threads=0):
     return oracle.attention(k, v, dt, q, st.first_pos, wl.n_kv_heads, st.ctx_len, rows=rows,
                             sm_scale=wl.sm_scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
                             n_threads=n_threads)
+
+
+def gpu_v_layout(v_rows: np.ndarray, vb: int) -> np.ndarray:
+    """Rearrange V given as [..., positions, D] (positions a multiple of vb)
+    into the device layout [..., positions/vb, D, vb]."""
+    *lead, n, d = v_rows.shape
+    x = v_rows.reshape(*lead, n // vb, vb, d)
+    return np.swapaxes(x, -1, -2)

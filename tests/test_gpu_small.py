@@ -14,7 +14,7 @@ import paged_kv_cache_addressing_amd as pa
 import workloads
 from paged_kv_cache_addressing_amd.resident import upload
 from tests._gpu import decode, launch_error, prefill, references, same_bytes, say, tol
-from tests._util import bits16, oracle_logical, oracle_pool
+from tests._util import bits16, gpu_v_layout, oracle_logical, oracle_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -49,13 +49,19 @@ def test_write_kv_bytes_match_oracle_store(dtype, d):
                          layouts=["paged", "slab", "paged"], n_pages=8, seed=5)
     say(f"write_kv {dtype} D={d}")
     res = upload(wl)
-    kp, vp = oracle_pool(wl)
+    vb = pa.v_block(dtype)
+    kp, vp = oracle_pool(wl)  # [pages][Hkv][256][D], the pages' head-major layout
     assert np.array_equal(np_bits(res.cache.k_pages), kp)
-    assert np.array_equal(np_bits(res.cache.v_pages), vp.transpose(0, 1, 3, 2))
-    k_log, v_log = oracle_logical(wl, 1)
+    assert np.array_equal(np_bits(res.cache.v_pages), gpu_v_layout(vp, vb))
+    k_log, v_log = oracle_logical(wl, 1)  # [300][Hkv][D]
     ks, vs = res.slabs[1]
-    assert np.array_equal(np_bits(ks)[:, :300, :], k_log.transpose(1, 0, 2))
-    assert np.array_equal(np_bits(vs)[:, :, :300], v_log.transpose(1, 2, 0))
+    cap = ks.shape[1]
+    k_full = np.zeros((2, cap, d), k_log.dtype)
+    v_full = np.zeros((2, cap, d), v_log.dtype)
+    k_full[:, :300] = k_log.transpose(1, 0, 2)
+    v_full[:, :300] = v_log.transpose(1, 0, 2)
+    assert np.array_equal(np_bits(ks), k_full)
+    assert np.array_equal(np_bits(vs), gpu_v_layout(v_full, vb))
 
 
 @pytest.mark.parametrize("scale", [1.0, 0.0107421875, 3.7])
@@ -76,7 +82,7 @@ def test_fp8_store_every_finite_bf16_value(scale):
     want_k = oracle.e4m3_encode(x32, scale).reshape(510, 128)
     want_v = oracle.e4m3_encode(x32, scale * 2).reshape(510, 128)
     got_k = ks.cpu().numpy()[0, :510, :]
-    got_v = vs.cpu().numpy()[0, :, :510].T
+    got_v = np.swapaxes(vs.cpu().numpy()[0], -1, -2).reshape(512, 128)[:510]
     bad = np.nonzero(got_k != want_k)
     assert bad[0].size == 0, (x32.reshape(510, 128)[bad][:8], got_k[bad][:8], want_k[bad][:8])
     assert np.array_equal(got_v, want_v)
@@ -249,3 +255,55 @@ def test_prefill_stream_alone_equals_beside_others():
         torch.cuda.synchronize()
         r0, r1 = st.row_offset, st.row_offset + st.n_rows
         assert same_bytes(out[r0:r1], both[r0:r1])
+
+
+# ----------------------------------------------------------------------------- partials + merge
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_decode_partials_match_oracle_split_form(dtype):
+    """The workspace triples follow the documented layout and equal the
+    oracle's split form (m in log2 units), and merge(partials) == decode."""
+    split = 1024
+    wl = workloads.build("halves", n_q_heads=12, n_kv_heads=2, head_dim=128, kv_dtype=dtype,
+                         ctx_lens=[2500, 1030], n_rows=[3, 16], seed=61, split_keys=split)
+    res = upload(wl)
+    full = decode(res)
+    ws = pa.decode_workspace(res.cache, res.streams, wl.n_q_heads, split)
+    ws.fill_(0xFF)  # every byte the merge reads must be written by the partials
+    pa.paged_attn_decode_partials(res.cache, res.streams, res.q, ws, sm_scale=res.sm_scale,
+                                  split_keys=split)
+    out = torch.empty_like(full)
+    pa.paged_attn_decode_merge(res.cache, res.streams, out, ws, split_keys=split)
+    torch.cuda.synchronize()
+    assert same_bytes(out, full)
+    kp, vp = oracle_pool(wl)
+    ps = wl.n_kv_heads * 256 * wl.head_dim
+    d, hq = wl.head_dim, wl.n_q_heads
+    slots = sum(st.n_rows * hq * -(-(st.first_pos + st.n_rows) // split) for st in wl.streams)
+    wsf = ws.view(torch.float32).cpu().numpy()
+    o_all = wsf[:slots * d].reshape(slots, d)
+    ml_off = -(-(slots * d * 4) // 256) * 256 // 4
+    ml = wsf[ml_off:ml_off + 2 * slots].reshape(slots, 2)
+    base = 0
+    for st in wl.streams:
+        ns = -(-(st.first_pos + st.n_rows) // split)
+        q = bits16(wl.q[st.row_offset:st.row_offset + st.n_rows])
+        m, l, o = oracle.attention_split(kp, vp, oracle.DTYPE_BF16 if dtype == "bf16" else
+                                         oracle.DTYPE_E4M3, q, st.first_pos, wl.n_kv_heads,
+                                         st.ctx_len, split, ns, page_table=st.pages,
+                                         page_stride=ps, sm_scale=wl.sm_scale,
+                                         k_scale=wl.k_scale, v_scale=wl.v_scale)
+        n = st.n_rows * hq * ns
+        gm = ml[base:base + n, 0].reshape(st.n_rows, hq, ns)
+        gl = ml[base:base + n, 1].reshape(st.n_rows, hq, ns)
+        go = o_all[base:base + n].reshape(st.n_rows, hq, ns, d)
+        masked = np.isneginf(m)
+        assert np.array_equal(np.isneginf(gm), masked)
+        assert (gl[masked] == 0).all() and (go[masked] == 0).all()
+        vis = ~masked
+        np.testing.assert_allclose(gm[vis], m[vis] / np.log(2.0), rtol=0, atol=2e-2)
+        np.testing.assert_allclose(gl[vis], l[vis], rtol=2e-2)
+        vs = wl.v_scale if dtype == "fp8" else 1.0  # o is kept in V-code units
+        np.testing.assert_allclose(go[vis] / gl[vis][..., None] * vs, o[vis] / l[vis][..., None],
+                                   rtol=0, atol=(2e-2 if dtype == "bf16" else 6e-2))
+        base += n
