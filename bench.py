@@ -251,6 +251,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--profile", choices=["decode", "prefill", "copy", "verify", "fp8"])
+    ap.add_argument("--only", choices=["prefill"],
+                    help="time one secondary workload only and print its record")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1",
@@ -261,6 +263,15 @@ def main():
 
     import workloads
     torch.cuda.set_device(0)
+
+    if args.only == "prefill":
+        wl4 = workloads.config4()
+        p = run_prefill(wl4, args.steps, args.warmup)
+        fl = attn_flops(wl4)
+        tf = fl / (p["prefill_ms"] * 1e-3) / 1e12
+        print(json.dumps({"prefill_ms": round(p["prefill_ms"], 4), "tflops": round(tf, 2),
+                          "frac": round(tf / BF16_PEAK_TFLOPS, 4)}), flush=True)
+        return
 
     if args.profile:  # a short run for rocprofv3: the named kernels only
         if args.profile == "copy":

@@ -10,14 +10,13 @@
 #include <utility>
 #include <vector>
 
-#include "../../include/paged_attn.h"
+#include "paged_attn.h"
 #include "pa_internal.hpp"
 
 namespace {
 
 using pa::kMaxLaunchStreams;
 using pa::kPage;
-using pa::kPrefillRows;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -428,6 +427,16 @@ int paged_attn_prefill(const pa_kv_cache* cache, const pa_stream* streams, int32
   if (live.empty()) return PA_OK;
   if (!q || !out) return PA_EINVAL;
   const float ks = cache->dtype == PA_KV_FP8_E4M3 ? cache->k_scale : 1.f;
+  const int32_t group = n_q_heads / cache->n_kv_heads;
+  // Columns per wave = rows per wave x heads per workgroup: take the largest
+  // divisor of the group that divides the column count (no idle columns), so
+  // the workgroup's K/V tiles serve as many q heads as possible.
+  const int32_t cols = pa::prefill_columns(cache->head_dim);
+  int32_t hw = 1;
+  for (int32_t d = 1; d <= group && d <= cols; ++d)
+    if (group % d == 0 && cols % d == 0) hw = d;
+  const int32_t rpw = cols / hw;  // rows per wave
+  const int32_t rpt = 4 * rpw;    // rows per workgroup tile
   for (size_t at = 0; at < live.size(); at += kMaxLaunchStreams) {
     pa::PrefillArgs A;
     std::memset(&A, 0, sizeof A);
@@ -435,17 +444,20 @@ int paged_attn_prefill(const pa_kv_cache* cache, const pa_stream* streams, int32
     A.out = static_cast<uint16_t*>(out);
     A.cache = cache_arg(cache);
     A.n_q_heads = n_q_heads;
-    A.group = n_q_heads / cache->n_kv_heads;
+    A.group = group;
+    A.heads_per_wg = hw;
+    A.rows_per_wave = rpw;
     A.scale_log2 = sm_scale * ks * kLog2e;
     A.v_scale = cache->dtype == PA_KV_FP8_E4M3 ? cache->v_scale : 1.f;
     int32_t tiles = 0;
     for (size_t j = at; j < live.size() && j < at + kMaxLaunchStreams; ++j) {
       pa::StreamArg a = stream_arg(cache, streams[live[j]]);
       a.block_begin = tiles;
-      tiles += (a.n_rows + kPrefillRows - 1) / kPrefillRows;
+      tiles += (a.n_rows + rpt - 1) / rpt;
       A.s[A.n_streams++] = a;
     }
     A.total_tiles = tiles;
+    A.xcd_remap = ((int64_t)tiles * n_q_heads / hw) % 8 == 0 ? 1 : 0;
     rc = pa::launch_prefill(A, cache->dtype, cache->head_dim, (hipStream_t)hip_stream);
     if (rc != 0) return rc;
   }

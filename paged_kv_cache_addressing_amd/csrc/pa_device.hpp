@@ -50,8 +50,10 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// Two floats -> two bf16 (RNE) in one register: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef float v2f __attribute__((__vector_size__(2 * sizeof(float))));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2bf));
 }
 
 // Keep the first `nv` 16-bit elements of an 8 x bf16 vector, zero the rest.
@@ -104,7 +106,7 @@ constexpr int v_block() { return 64 / ESZ; }
 
 // Element offset of V(j, d) inside a tile.
 template <int D, int ESZ>
-__device__ __forceinline__ int v_off(int j, int d) {
+__host__ __device__ __forceinline__ int v_off(int j, int d) {
   constexpr int VB = v_block<ESZ>();
   return ((j / VB) * D + d) * VB + (j % VB);
 }
@@ -114,7 +116,10 @@ __device__ __forceinline__ PageTile page_tile(const StreamArg& s, const CacheArg
                                               int g) {
   PageTile r;
   if (s.layout == 0) {
-    int32_t page = __builtin_amdgcn_readfirstlane(s.page_table[t]);
+    // Scalar load through the constant address space: tracked by lgkmcnt, so
+    // it never waits on (or drains) the vector loads in flight.
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    const int32_t page = ((const_i32*)s.page_table)[t];
     r.ok = (uint32_t)page < (uint32_t)c.n_pages;
     int64_t base = (int64_t)(r.ok ? page : 0) * c.page_stride + (int64_t)g * kPage * D;
     r.k = s.k_base + base * ESZ;

@@ -9,7 +9,10 @@ namespace pa {
 
 constexpr int kPage = 256;            // positions per page (compile-time everywhere)
 constexpr int kMaxLaunchStreams = 32; // streams per kernel launch; calls are chunked
-constexpr int kPrefillRows = 128;     // query rows per prefill workgroup
+
+// 16-column MFMA n-tiles per prefill wave: 3 (48 columns) where the O^T
+// accumulators fit beside Q^T and two S tiles, 2 (32 columns) at head_dim 256.
+constexpr int prefill_ntiles(int head_dim) { return head_dim >= 256 ? 2 : 3; }
 
 struct StreamArg {
   int32_t layout;       // 0 paged, 1 slab
@@ -59,7 +62,10 @@ struct PrefillArgs {
   int32_t n_q_heads;
   int32_t group;
   int32_t n_streams;
-  int32_t total_tiles;  // row tiles in this launch
+  int32_t total_tiles;    // row tiles in this launch (per kv head)
+  int32_t heads_per_wg;   // q heads of the group a workgroup covers (divides group)
+  int32_t rows_per_wave;  // rows a wave covers (columns = rows_per_wave * heads_per_wg)
+  int32_t xcd_remap;      // 1: map blocks so each XCD runs one contiguous range
   float scale_log2;
   float v_scale;
   StreamArg s[kMaxLaunchStreams];
