@@ -251,7 +251,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--profile", choices=["decode", "prefill", "copy", "verify", "fp8"])
-    ap.add_argument("--only", choices=["prefill"],
+    ap.add_argument("--only", choices=["prefill", "verify", "fp8"],
                     help="time one secondary workload only and print its record")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -271,6 +271,18 @@ def main():
         tf = fl / (p["prefill_ms"] * 1e-3) / 1e12
         print(json.dumps({"prefill_ms": round(p["prefill_ms"], 4), "tflops": round(tf, 2),
                           "frac": round(tf / BF16_PEAK_TFLOPS, 4)}), flush=True)
+        return
+
+    if args.only in ("verify", "fp8"):
+        w = workloads.config5() if args.only == "verify" else workloads.config3()
+        rr, _, _ = run_decode(w, args.steps, args.warmup, with_store=args.only == "fp8")
+        nb, fl = kv_bytes(w), attn_flops(w)
+        print(json.dumps({"workload": w.name, "partial_ms": round(rr["partial_ms"], 5),
+                          "merge_ms": round(rr["merge_ms"], 5),
+                          "frac_hbm_partial": round(nb / (rr["partial_ms"] * 1e-3) / 1e9 /
+                                                    HBM_PEAK_GBS, 4),
+                          "tflops_partial": round(fl / (rr["partial_ms"] * 1e-3) / 1e12, 2)}),
+              flush=True)
         return
 
     if args.profile:  # a short run for rocprofv3: the named kernels only

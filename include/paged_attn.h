@@ -32,8 +32,10 @@
  *     are rows row_offset .. row_offset + n_rows - 1.  Query head h reads kv
  *     head h / (n_q_heads / n_kv_heads).
  *   - Page ids read from a device page table are checked on the device: an
- *     id outside [0, n_pages) is never dereferenced; attention rows that
- *     would read it produce NaN and write_kv skips the row.
+ *     id outside [0, n_pages) is never dereferenced.  Attention rows that
+ *     would read it come out NaN (so may other rows of the same stream that
+ *     one workgroup computes with them); other streams are unaffected.
+ *     write_kv skips a row whose page id is rejected.
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
@@ -177,6 +179,12 @@ PA_API int write_kv(const pa_kv_cache *cache, const pa_stream *streams, int32_t 
  * out = v_scale * sum_j e^(m_j-M) o_j / sum_j e^(m_j-M) l_j  as bf16 (RNE).
  * The split count of a stream depends on that stream alone, so a stream's
  * output bytes do not depend on the other streams in the call.
+ * Which kernel computes a stream's partials depends on that stream alone
+ * too: a stream with at most 32 (row, q head) pairs per kv head (for a group
+ * of 6, up to 5 rows) streams K/V from HBM into registers, one 16-column
+ * MFMA tile per workgroup; a wider one (verify rows) runs on the row-tile
+ * kernel, one workgroup per (split, kv head) whose LDS K/V tiles serve every
+ * row and q head of the group, so each split is read from HBM once.
  * n_rows per stream <= PA_DECODE_MAX_ROWS; sm_scale > 0 (1/sqrt(head_dim)
  * is the usual value); split_keys a positive multiple of 256.
  * The workspace (device, >= paged_attn_decode_workspace_size bytes, 256-byte
@@ -193,10 +201,14 @@ PA_API int paged_attn_decode(const pa_kv_cache *cache, const pa_stream *streams,
  * between them (for example partials computed on several devices for one
  * stream's key shards and gathered into one workspace before the merge).
  * paged_attn_decode_partials writes every (row, q head, split) triple of the
- * call into the workspace: o (fp32 [D], unnormalised, in units of the stored
- * V values: the merge applies v_scale for fp8), m (fp32, log2 units:
- * the split's largest logit times log2(e)) and l (fp32).  A split wholly
- * masked for a row stores m = -inf, l = 0, o = 0.  Triple (r, h, j) of the
+ * call into the workspace: m (fp32, a reference logit in log2 units), then
+ * l = sum_t 2^(s_t - m) and o = sum_t 2^(s_t - m) v_t over the split's
+ * visible keys t, with s_t the logit times log2(e), o (fp32 [D]) in units of
+ * the stored V values (the merge applies v_scale for fp8).  m is the split's
+ * largest s_t for narrow streams and lies at most 8 below it for wide ones
+ * (their running maximum moves only when a logit passes it by more than 8),
+ * so every term is at most 2^8.  A split wholly masked for a row stores
+ * m = -inf, l = 0, o = 0.  Triple (r, h, j) of the
  * i-th stream lives at slot  S_i + (r*n_q_heads + h)*n_splits_i + j, where S_i
  * is the sum of n_rows*n_q_heads*n_splits over earlier streams; o at float
  * offset slot*head_dim, (m, l) at the second region (byte offset
@@ -219,12 +231,12 @@ PA_API int paged_attn_decode_merge(const pa_kv_cache *cache, const pa_stream *st
  * be NULL), and the totals.  Host only; validates like paged_attn_decode
  * minus the device pointers. */
 typedef struct pa_decode_plan {
-  int32_t n_launch_groups;   /* kernel pairs enqueued (streams are grouped) */
+  int32_t n_launch_groups;   /* launch groups (streams are grouped, at most 32 a group) */
   int32_t total_splits;      /* sum over streams of their split counts */
-  int32_t col_tiles;         /* 16-column MFMA tiles per (split, kv head) */
-  int32_t partial_blocks;    /* workgroups of the partial kernel(s) */
+  int32_t col_tiles;         /* 16-column MFMA tiles per (split, kv head), narrow streams */
+  int32_t partial_blocks;    /* workgroups of all partial kernels */
   int32_t merge_blocks;      /* workgroups of the merge kernel(s) */
-  int32_t reserved;
+  int32_t wide_blocks;       /* of partial_blocks: those of the LDS-shared row-tile kernel */
   size_t workspace_bytes;
 } pa_decode_plan;
 
@@ -235,10 +247,11 @@ PA_API int paged_attn_decode_plan(const pa_stream *streams, int32_t n_streams, i
 /* ----------------------------------------------------------------- prefill
  * Prompt-chunk prefill (pull request #1373, prompt rows; pull request #2011,
  * hpattn_p256_kernel): every row of every stream, causal against the
- * stream's stored prefix, one launch, page size 256 fixed.  Rows are tiled
- * 128 at a time within a stream (tiles never span streams); a row's bytes do
- * not depend on which other rows share its tile, so any slicing of a
- * stream's rows into calls gives the same bytes as one call. */
+ * stream's stored prefix, one launch, page size 256 fixed.  A workgroup
+ * covers a tile of a stream's rows for some q heads of one kv head (tiles
+ * never span streams); a row's bytes do not depend on which other rows
+ * share its tile, so any slicing of a stream's rows into calls gives the
+ * same bytes as one call. */
 PA_API int paged_attn_prefill(const pa_kv_cache *cache, const pa_stream *streams, int32_t n_streams,
                        const void *q, void *out, int32_t n_q_heads, float sm_scale,
                        void *hip_stream);

@@ -25,10 +25,17 @@ COMMON = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 
-# Per-source flags.  prefill.hip never tests for NaN (masked keys are
-# replaced by a select before any max), so NaN canonicalisation of max
-# inputs is dropped there.
-EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
+# Per-source flags for prefill.hip (the row-tile kernel):
+#  * it never tests for NaN (masked keys are replaced by a select before any
+#    max, and rejected pages are flagged with NaN bit patterns written as
+#    integers), so NaN canonicalisation of max inputs is dropped;
+#  * its MFMA accumulators are selected in VGPR form.  In AGPR form the
+#    compiler kept a VGPR copy of every O^T accumulator for the (rare) VALU
+#    rescale and moved all of them between the two files on every step
+#    (about 300 v_accvgpr moves per 64 MFMAs); in VGPR form the accumulators
+#    stay put and only the loop-invariant Q^T operands overflow into AGPRs,
+#    which the MFMAs read directly.
+EXTRA = {"prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False, resource_usage: bool = False) -> str:

@@ -146,9 +146,52 @@ size_t ws_bytes(int64_t total_slots, int32_t head_dim) {
          align256((size_t)total_slots * 2 * sizeof(float));
 }
 
+// Row tiling of the row-tile kernel: a workgroup covers `heads` q heads of
+// one kv head (a divisor of the group) and `rows` rows, its 4 waves holding
+// 4 * columns-per-wave (row, head) columns.
+struct RowTiling {
+  int32_t heads;
+  int32_t rows;
+};
+
+// Prefill: the largest divisor of the group that also divides a wave's
+// column count, so no wave holds a partial row and the workgroup's K/V
+// tiles serve as many q heads as that allows.
+RowTiling prefill_tiling(int32_t head_dim, int32_t group) {
+  const int32_t cols = pa::prefill_columns(head_dim);
+  int32_t hw = 1;
+  for (int32_t d = 1; d <= group && d <= cols; ++d)
+    if (group % d == 0 && cols % d == 0) hw = d;
+  return {hw, 4 * cols / hw};
+}
+
+// Decode streams with many columns: the largest divisor of the group that
+// fits the workgroup's columns (the whole group whenever it fits), so every
+// split's K/V is read by as few workgroups as possible.
+RowTiling wide_tiling(int32_t head_dim, int32_t group) {
+  const int32_t cols = 4 * pa::prefill_columns(head_dim);
+  int32_t hw = 1;
+  for (int32_t d = 1; d <= group && d <= cols; ++d)
+    if (group % d == 0) hw = d;
+  return {hw, cols / hw};
+}
+
+// A decode stream whose (row, q head) columns per kv head exceed two MFMA
+// column tiles runs on the row-tile kernel in split mode, where one
+// workgroup's LDS tiles feed all its columns; narrower streams keep the
+// register-streaming partial kernel.  The choice depends on the stream
+// alone, so its bytes do not depend on the rest of the batch.
+constexpr int32_t kWideColumns = 32;
+bool wide_stream(const pa_stream& t, int32_t group) {
+  return (int64_t)t.n_rows * group > kWideColumns;
+}
+
+// Column tiles of the register-streaming partial kernel for a launch group:
+// enough for its widest narrow stream.
 int32_t col_tiles_of(const pa_stream* s, const std::vector<int32_t>& grp, int32_t group) {
   int32_t mr = 0;
-  for (int32_t i : grp) mr = std::max(mr, s[i].n_rows);
+  for (int32_t i : grp)
+    if (!wide_stream(s[i], group)) mr = std::max(mr, s[i].n_rows);
   return (group * mr + 15) / 16;
 }
 
@@ -286,17 +329,23 @@ int paged_attn_decode_plan(const pa_stream* streams, int32_t n_streams, int32_t 
   if (plan) {
     std::memset(plan, 0, sizeof *plan);
     const int32_t group = n_q_heads / n_kv_heads;
+    const RowTiling W = wide_tiling(head_dim, group);
     plan->n_launch_groups = (int32_t)P.groups.size();
     for (const auto& grp : P.groups) {
-      int32_t ts = 0, tr = 0;
+      int32_t tr = 0, narrow_splits = 0, wide_items = 0;
       for (int32_t i : grp) {
-        ts += P.splits[i];
+        plan->total_splits += P.splits[i];
         tr += streams[i].n_rows;
+        if (wide_stream(streams[i], group))
+          wide_items += (streams[i].n_rows + W.rows - 1) / W.rows * P.splits[i];
+        else
+          narrow_splits += P.splits[i];
       }
       const int32_t ct = col_tiles_of(streams, grp, group);
-      plan->total_splits += ts;
+      const int32_t wb = wide_items * n_kv_heads * (group / W.heads);
       plan->col_tiles = std::max(plan->col_tiles, ct);
-      plan->partial_blocks += ts * ct * n_kv_heads;
+      plan->partial_blocks += narrow_splits * ct * n_kv_heads + wb;
+      plan->wide_blocks += wb;
       plan->merge_blocks += tr * n_q_heads;
     }
     plan->workspace_bytes = ws_bytes(P.total_slots, head_dim);
@@ -308,12 +357,21 @@ int paged_attn_decode_plan(const pa_stream* streams, int32_t n_streams, int32_t 
 
 namespace {
 
-// Validate a decode call and build one kernel-argument block per launch
+// The kernels of one decode launch group: the register-streaming partial
+// kernel over its narrow streams, the row-tile kernel in split mode over its
+// wide streams (either may have no streams), and the merge over all of them.
+struct DecodeLaunch {
+  pa::DecodeArgs narrow;
+  pa::PrefillArgs wide;
+  pa::DecodeArgs merge;
+};
+
+// Validate a decode call and build the kernel arguments of every launch
 // group.  `need_q` / `need_out` say which of q and out the caller uses.
 int prepare_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n_streams,
                    const void* q, void* out, int32_t n_q_heads, float sm_scale,
                    int32_t split_keys, void* workspace, size_t workspace_bytes, bool need_q,
-                   bool need_out, std::vector<pa::DecodeArgs>& launches) {
+                   bool need_out, std::vector<DecodeLaunch>& launches) {
   launches.clear();
   int rc = check_call(cache, streams, n_streams, n_q_heads, PA_DECODE_MAX_ROWS);
   if (rc != PA_OK) return rc;
@@ -331,9 +389,13 @@ int prepare_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n
                                                    sizeof(float)));
   const int32_t group = n_q_heads / cache->n_kv_heads;
   const float ks = cache->dtype == PA_KV_FP8_E4M3 ? cache->k_scale : 1.f;
+  const float scale_log2 = sm_scale * ks * kLog2e;
+  const float vs = cache->dtype == PA_KV_FP8_E4M3 ? cache->v_scale : 1.f;
+  const RowTiling W = wide_tiling(cache->head_dim, group);
   for (const auto& grp : P.groups) {
-    pa::DecodeArgs A;
-    std::memset(&A, 0, sizeof A);
+    DecodeLaunch D;
+    std::memset(&D, 0, sizeof D);
+    pa::DecodeArgs& A = D.merge;
     A.q = static_cast<const uint16_t*>(q);
     A.out = static_cast<uint16_t*>(out);
     A.ws_o = ws_o;
@@ -342,25 +404,60 @@ int prepare_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n
     A.n_q_heads = n_q_heads;
     A.group = group;
     A.split_keys = split_keys;
-    A.scale_log2 = sm_scale * ks * kLog2e;
-    A.v_scale = cache->dtype == PA_KV_FP8_E4M3 ? cache->v_scale : 1.f;
+    A.scale_log2 = scale_log2;
+    A.v_scale = vs;
     A.col_tiles = col_tiles_of(streams, grp, group);
-    int32_t splits = 0, rows = 0;
+    D.narrow = A;
+    pa::PrefillArgs& B = D.wide;
+    B.q = A.q;
+    B.ws_o = ws_o;
+    B.ws_ml = ws_ml;
+    B.cache = A.cache;
+    B.n_q_heads = n_q_heads;
+    B.group = group;
+    B.heads_per_wg = W.heads;
+    B.rows_per_tile = W.rows;
+    B.split_keys = split_keys;
+    B.scale_log2 = scale_log2;
+    B.v_scale = vs;
+    int32_t splits = 0, rows = 0, items = 0;
     for (int32_t i : grp) {
       pa::StreamArg a = stream_arg(cache, streams[i]);
       a.n_splits = P.splits[i];
-      a.block_begin = splits;
       a.row_begin = rows;
       a.slot_base = P.slot_base[i];
-      splits += a.n_splits;
       rows += a.n_rows;
       A.s[A.n_streams++] = a;
+      if (wide_stream(streams[i], group)) {
+        a.block_begin = items;
+        items += (a.n_rows + W.rows - 1) / W.rows * a.n_splits;
+        B.s[B.n_streams++] = a;
+      } else {
+        a.block_begin = splits;
+        splits += a.n_splits;
+        D.narrow.s[D.narrow.n_streams++] = a;
+      }
     }
-    A.total_splits = splits;
     A.total_rows = rows;
-    launches.push_back(A);
+    D.narrow.total_splits = splits;
+    B.total_tiles = items;
+    launches.push_back(D);
   }
   return PA_OK;
+}
+
+// Enqueue the partial kernels of one launch group.
+int launch_partials(const DecodeLaunch& D, const pa_kv_cache* cache, hipStream_t st) {
+  if (D.narrow.n_streams > 0) {
+    const int rc = pa::launch_decode_partials(D.narrow, cache->dtype, cache->head_dim,
+                                              cache->n_kv_heads, st);
+    if (rc != 0) return rc;
+  }
+  if (D.wide.n_streams > 0) {
+    const int rc = pa::launch_prefill(D.wide, cache->dtype, cache->head_dim, st);
+    if (rc != 0) return rc;
+  }
+  return 0;
 }
 
 }  // namespace
@@ -371,13 +468,12 @@ int paged_attn_decode_partials(const pa_kv_cache* cache, const pa_stream* stream
                                int32_t n_streams, const void* q, int32_t n_q_heads,
                                float sm_scale, int32_t split_keys, void* workspace,
                                size_t workspace_bytes, void* hip_stream) {
-  std::vector<pa::DecodeArgs> L;
+  std::vector<DecodeLaunch> L;
   int rc = prepare_decode(cache, streams, n_streams, q, nullptr, n_q_heads, sm_scale,
                           split_keys, workspace, workspace_bytes, true, false, L);
   if (rc != PA_OK) return rc;
-  for (const auto& A : L) {
-    rc = pa::launch_decode_partials(A, cache->dtype, cache->head_dim, cache->n_kv_heads,
-                                    (hipStream_t)hip_stream);
+  for (const auto& D : L) {
+    rc = launch_partials(D, cache, (hipStream_t)hip_stream);
     if (rc != 0) return rc;
   }
   return PA_OK;
@@ -386,12 +482,12 @@ int paged_attn_decode_partials(const pa_kv_cache* cache, const pa_stream* stream
 int paged_attn_decode_merge(const pa_kv_cache* cache, const pa_stream* streams,
                             int32_t n_streams, void* out, int32_t n_q_heads, int32_t split_keys,
                             const void* workspace, size_t workspace_bytes, void* hip_stream) {
-  std::vector<pa::DecodeArgs> L;
+  std::vector<DecodeLaunch> L;
   int rc = prepare_decode(cache, streams, n_streams, nullptr, out, n_q_heads, 1.f, split_keys,
                           const_cast<void*>(workspace), workspace_bytes, false, true, L);
   if (rc != PA_OK) return rc;
-  for (const auto& A : L) {
-    rc = pa::launch_decode_merge(A, cache->head_dim, (hipStream_t)hip_stream);
+  for (const auto& D : L) {
+    rc = pa::launch_decode_merge(D.merge, cache->head_dim, (hipStream_t)hip_stream);
     if (rc != 0) return rc;
   }
   return PA_OK;
@@ -401,15 +497,14 @@ int paged_attn_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_
                       const void* q, void* out, int32_t n_q_heads, float sm_scale,
                       int32_t split_keys, void* workspace, size_t workspace_bytes,
                       void* hip_stream) {
-  std::vector<pa::DecodeArgs> L;
+  std::vector<DecodeLaunch> L;
   int rc = prepare_decode(cache, streams, n_streams, q, out, n_q_heads, sm_scale, split_keys,
                           workspace, workspace_bytes, true, true, L);
   if (rc != PA_OK) return rc;
-  for (const auto& A : L) {
-    rc = pa::launch_decode_partials(A, cache->dtype, cache->head_dim, cache->n_kv_heads,
-                                    (hipStream_t)hip_stream);
+  for (const auto& D : L) {
+    rc = launch_partials(D, cache, (hipStream_t)hip_stream);
     if (rc != 0) return rc;
-    rc = pa::launch_decode_merge(A, cache->head_dim, (hipStream_t)hip_stream);
+    rc = pa::launch_decode_merge(D.merge, cache->head_dim, (hipStream_t)hip_stream);
     if (rc != 0) return rc;
   }
   return PA_OK;
@@ -428,15 +523,7 @@ int paged_attn_prefill(const pa_kv_cache* cache, const pa_stream* streams, int32
   if (!q || !out) return PA_EINVAL;
   const float ks = cache->dtype == PA_KV_FP8_E4M3 ? cache->k_scale : 1.f;
   const int32_t group = n_q_heads / cache->n_kv_heads;
-  // Columns per wave = rows per wave x heads per workgroup: take the largest
-  // divisor of the group that divides the column count (no idle columns), so
-  // the workgroup's K/V tiles serve as many q heads as possible.
-  const int32_t cols = pa::prefill_columns(cache->head_dim);
-  int32_t hw = 1;
-  for (int32_t d = 1; d <= group && d <= cols; ++d)
-    if (group % d == 0 && cols % d == 0) hw = d;
-  const int32_t rpw = cols / hw;  // rows per wave
-  const int32_t rpt = 4 * rpw;    // rows per workgroup tile
+  const RowTiling T = prefill_tiling(cache->head_dim, group);
   for (size_t at = 0; at < live.size(); at += kMaxLaunchStreams) {
     pa::PrefillArgs A;
     std::memset(&A, 0, sizeof A);
@@ -445,19 +532,19 @@ int paged_attn_prefill(const pa_kv_cache* cache, const pa_stream* streams, int32
     A.cache = cache_arg(cache);
     A.n_q_heads = n_q_heads;
     A.group = group;
-    A.heads_per_wg = hw;
-    A.rows_per_wave = rpw;
+    A.heads_per_wg = T.heads;
+    A.rows_per_tile = T.rows;
     A.scale_log2 = sm_scale * ks * kLog2e;
     A.v_scale = cache->dtype == PA_KV_FP8_E4M3 ? cache->v_scale : 1.f;
     int32_t tiles = 0;
     for (size_t j = at; j < live.size() && j < at + kMaxLaunchStreams; ++j) {
       pa::StreamArg a = stream_arg(cache, streams[live[j]]);
       a.block_begin = tiles;
-      tiles += (a.n_rows + rpt - 1) / rpt;
+      tiles += (a.n_rows + T.rows - 1) / T.rows;
       A.s[A.n_streams++] = a;
     }
     A.total_tiles = tiles;
-    A.xcd_remap = ((int64_t)tiles * n_q_heads / hw) % 8 == 0 ? 1 : 0;
+    A.xcd_remap = ((int64_t)tiles * n_q_heads / T.heads) % 8 == 0 ? 1 : 0;
     rc = pa::launch_prefill(A, cache->dtype, cache->head_dim, (hipStream_t)hip_stream);
     if (rc != 0) return rc;
   }

@@ -55,16 +55,24 @@ struct DecodeArgs {
   StreamArg s[kMaxLaunchStreams];
 };
 
+// Row-tile kernel arguments.  Without split_keys it is prefill: each work
+// item is one tile of a stream's rows over all the keys they see, written as
+// normalised bf16 rows.  With split_keys > 0 it is the decode partial for
+// streams with many (row, q head) columns: each work item is one (row tile,
+// split) of a stream, written as (m, l, o) partials into the decode workspace.
 struct PrefillArgs {
   const uint16_t* q;
-  uint16_t* out;
+  uint16_t* out;          // prefill: bf16 [rows][Hq][D]
+  float* ws_o;            // split mode: [slots][D] unnormalised partial outputs
+  float* ws_ml;           // split mode: [slots][2] (m in log2 units, l)
   CacheArg cache;
   int32_t n_q_heads;
   int32_t group;
   int32_t n_streams;
-  int32_t total_tiles;    // row tiles in this launch (per kv head)
+  int32_t total_tiles;    // work items in this launch (per head group)
   int32_t heads_per_wg;   // q heads of the group a workgroup covers (divides group)
-  int32_t rows_per_wave;  // rows a wave covers (columns = rows_per_wave * heads_per_wg)
+  int32_t rows_per_tile;  // rows a workgroup covers: floor(4 * columns per wave / heads_per_wg)
+  int32_t split_keys;     // 0: prefill; > 0: split-K partials of this many keys
   int32_t xcd_remap;      // 1: map blocks so each XCD runs one contiguous range
   float scale_log2;
   float v_scale;

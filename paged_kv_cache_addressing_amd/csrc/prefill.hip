@@ -12,6 +12,13 @@
 // (row, q head) pair: NT = 2 at head_dim 256 (16 rows x 2 heads for a group of
 // 6), NT = 3 at 128.  The K/V tiles in LDS serve all HW heads, and the other
 // head groups of the same kv head run on the same XCD, so K/V also hit in L2.
+//
+// Split mode (decode streams with many rows, e.g. speculative verify rows):
+// the same kernel computes one 4,096-key split (any split_keys) of a row
+// tile covering the whole group (16 rows x 6 heads = 96 columns in three
+// waves), so each split's K/V is read from HBM once for all its columns, and
+// writes the split's (m, l, o) partial for the log-sum-exp merge (TensorFold
+// issue #1344, "Mechanism").
 //   S^T (32 keys x 16NT cols) = K Q^T    : 2 m-tiles x NT n-tiles x D/32 k-steps
 //   O^T (D x 16NT cols)      += V^T P^T  : D/16 m-tiles x NT n-tiles x 1 k-step
 // The key order inside a step is permuted so each lane's S^T C-rows are the
@@ -20,8 +27,9 @@
 // Pipeline.  K and V steps (32 keys) rotate through three LDS slots each, in
 // "fragment order" (the 1 KiB an MFMA operand needs is contiguous, lane l's
 // 16 bytes at l*16, so ds_read_b128 is conflict-free).  bf16 arrives by
-// global_load_lds_dwordx4 straight into LDS, two steps ahead; fp8 goes
-// through registers one step ahead and is converted to bf16 once.  In step v
+// global_load_lds_dwordx4 straight into LDS, two steps ahead; fp8 codes
+// arrive the same way into a staging ring three steps ahead and are
+// converted to bf16 fragment order once, one step ahead.  In step v
 // a wave computes S(v+1) = K(v+1) Q^T on the matrix cores while the VALU does
 // the softmax of S(v), then accumulates O += V(v) P(v).
 //
@@ -45,11 +53,8 @@ namespace pa {
 // (LDS-DMA loads included; they complete in issue order).
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else static_assert(N == 0, "unsupported count");
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Workgroup barrier for LDS hand-off only: this wave's LDS operations are
@@ -63,7 +68,8 @@ __device__ __forceinline__ void lds_barrier() {
 template <int KV, int D>
 __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   // A workgroup owns one kv head g, HW = heads_per_wg of its q heads (head
-  // group hg) and a tile of 4*rpw rows; a wave owns rpw rows x HW heads.
+  // group hg) and a tile of rpt rows: its 4*16*NT columns, numbered
+  // c = 16*NT*wave + 16*nt + n, are the (row, head) pairs (c / HW, c % HW).
   constexpr int ESZ = KV ? 1 : 2;
   constexpr int BK = 32;                // keys per step
   constexpr int MT = 2;                 // S^T m-tiles per step
@@ -77,11 +83,16 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   constexpr int NSLOT = 3;
   constexpr int KSLOT = KF * 64;        // 16-byte entries per slot
   constexpr int VSLOT = VF * 64;
-  constexpr int KLD = KF * 64 / 2 / 256;  // fp8: 16-byte K loads per thread per step
-  constexpr int VLD = VF * 64 / 256;      // fp8: 8-byte V loads per thread per step
+  // fp8: raw codes land in a staging ring (16-byte entries per step) and are
+  // converted to bf16 fragment order from there.
+  constexpr int KST = KF * 64 / 2;
+  constexpr int VST = VF * 64 / 2;
+  constexpr int NSTG = 3;
+  constexpr int K8PW = KST / 256;       // fp8 DMAs per wave per step
+  constexpr int V8PW = VST / 256;
   static_assert(kPage % BK == 0, "a step never straddles two pages");
 
-  __shared__ v4u lds[NSLOT * (KSLOT + VSLOT)];
+  __shared__ v4u lds[NSLOT * (KSLOT + VSLOT) + (KV ? NSTG * (KST + VST) : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,44 +101,52 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   const int a = lane >> 4;
   const int G = A.group;
   const int HW = A.heads_per_wg;
-  const int rpw = A.rows_per_wave;
-  const int rpt = 4 * rpw;
+  const int rpt = A.rows_per_tile;
+  const bool split_mode = A.split_keys > 0;
 
-  // Logical work item: (kv head, head group) major, row tiles longest first.
-  // With the remap, the blocks one XCD runs (blockIdx % 8 picks the XCD) form
-  // one contiguous logical range, i.e. one kv head, whose K/V then hit in L2.
+  // Logical work item: (kv head, head group) major, then items (prefill:
+  // row tiles longest first; split mode: (row tile, split) in order).  With
+  // the remap, the blocks one XCD runs (blockIdx % 8 picks the XCD) form one
+  // contiguous logical range, i.e. one kv head, whose K/V then hit in L2.
   const int nb = gridDim.x;
   const int L = A.xcd_remap ? (int)(blockIdx.x % 8) * (nb / 8) + (int)(blockIdx.x / 8)
                             : (int)blockIdx.x;
   const int hgrp = L / A.total_tiles;      // kv head * (G / HW) + head group
   const int g = hgrp / (G / HW);
   const int h0 = g * G + (hgrp % (G / HW)) * HW;
-  const int tg = A.total_tiles - 1 - L % A.total_tiles;
-  const int si = find_stream<0>(A.s, A.n_streams, tg);
+  const int it = split_mode ? L % A.total_tiles : A.total_tiles - 1 - L % A.total_tiles;
+  const int si = find_stream<0>(A.s, A.n_streams, it);
   const StreamArg& S = A.s[si];
-  const int row0 = (tg - S.block_begin) * rpt;
+  const int local = it - S.block_begin;
+  const int tile = split_mode ? local / S.n_splits : local;
+  const int split = split_mode ? local - tile * S.n_splits : 0;
+  const int row0 = tile * rpt;
   const int rows_here = min(rpt, S.n_rows - row0);
   const int pos_first = S.first_pos + row0;
   const int pos_last = pos_first + rows_here - 1;
-  const int n_keys_t = pos_last + 1;
-  const int n_st = (n_keys_t + BK - 1) / BK;
-  const bool wave_active = wave * rpw < rows_here;
+  const int n_keys_t = pos_last + 1;       // keys the tile's last row sees
+  // Steps [v_lo, v_hi) of 32 keys: all keys the tile sees, or one split of them.
+  const int k_lo = split * A.split_keys;
+  const int k_end = split_mode ? min(k_lo + A.split_keys, n_keys_t) : n_keys_t;
+  const int v_lo = k_lo / BK;
+  const int v_hi = k_end > k_lo ? (k_end + BK - 1) / BK : v_lo;
+  const bool wave_active = wave * 16 * NT < rows_here * HW;
 
-  // Columns of this wave: lc = 16*nt + n -> (local row lc / HW, head lc % HW).
+  // Columns of this wave.
   int crow[NT], chead[NT], cpos[NT];
   bool cok[NT];
   v8bf qb[NT][KS];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int lc = 16 * nt + n;
-    const int rl = lc / HW;
-    chead[nt] = h0 + (lc - rl * HW);
-    crow[nt] = row0 + wave * rpw + rl;
-    cok[nt] = rl < rpw && crow[nt] < row0 + rows_here;
+    const int c = 16 * NT * wave + 16 * nt + n;
+    const int rl = c / HW;
+    chead[nt] = h0 + (c - rl * HW);
+    crow[nt] = row0 + rl;
+    cok[nt] = rl < rows_here;
     cpos[nt] = cok[nt] ? S.first_pos + crow[nt] : pos_last;
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(A.q) +
                         ((int64_t)(S.row_offset + (cok[nt] ? crow[nt] : row0)) * A.n_q_heads +
-                         chead[nt]) * D * 2;
+                         (cok[nt] ? chead[nt] : h0)) * D * 2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = KV ? 64 * (ks >> 1) + 16 * a + 8 * (ks & 1) : 32 * ks + 8 * a;
@@ -210,53 +229,62 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
     }
   };
 
-  // fp8 loaders: HBM -> registers at issue, convert + ds_write at commit.
-  v4u st_k[KV ? KLD : 1];
-  v2u st_v[KV ? VLD : 1];
-  auto issue_fp8 = [&](int vk, int vv) {
-    if (vk >= 0) {
-      const PageTile& T = page_k(vk);
-      const int o = (vk & 7) * BK;
+  // fp8 loaders.  Raw codes are DMAed into the staging ring (K four steps
+  // and V three steps before their use), each 16-byte entry by the wave that
+  // converts it; the conversion to bf16 fragment order then runs one step
+  // ahead of use (K two steps).  Every E4M3FN value is a bf16 value, so the
+  // conversion is exact.
+  v4u* const Sbase = lds + NSLOT * (KSLOT + VSLOT);
+  auto dma8_k = [&](int v) {
+    const PageTile& T = page_k(v);
+    const uint8_t* base = T.k + (int64_t)(v & 7) * BK * D;
+    v4u* dst = Sbase + (v % NSTG) * (KST + VST);
 #pragma unroll
-      for (int i = 0; i < KLD; ++i) {
-        const int q = i * 256 + tid, lp = q & 63, fp = q >> 6, m = lp & 15;
-        const int mt = fp / (KS / 2), kq = fp % (KS / 2);
-        st_k[i] = load16(T.k + (int64_t)(o + 8 * (m >> 2) + (m & 3) + 4 * mt) * D + 64 * kq +
-                         16 * (lp >> 4));
-      }
-    }
-    if (vv >= 0) {
-      const PageTile& T = page_v(vv);
-      const int o = (vv & 7) * BK;
-#pragma unroll
-      for (int i = 0; i < VLD; ++i) {
-        const int q = i * 256 + tid, lp = q & 63, md = q >> 6;
-        st_v[i] = *reinterpret_cast<const v2u*>(
-            T.v + v_off<D, ESZ>(o + 8 * (lp >> 4), 16 * md + (lp & 15)));
-      }
+    for (int i = 0; i < K8PW; ++i) {
+      // entry fp*64 + lane: 16 dims (two QK k-steps) of one S^T row
+      const int fp = 4 * i + wave, mt = fp / (KS / 2), kq = fp % (KS / 2);
+      const int off = (krow + 4 * mt) * D + 64 * kq + 16 * a;
+      __builtin_amdgcn_global_load_lds(base + off, dst + fp * 64, 16, 0, 0);
     }
   };
-  auto commit_fp8 = [&](int vk, int vv) {
+  auto dma8_v = [&](int v) {
+    const PageTile& T = page_v(v);
+    const int o = (v & 7) * BK;
+    v4u* dst = Sbase + (v % NSTG) * (KST + VST) + KST;
+#pragma unroll
+    for (int i = 0; i < V8PW; ++i) {
+      // entry q: 16 keys (half h of the step) of dim 16*md + dl
+      // (the offset is named first: a call nested in the builtin's argument
+      // list makes the host pass drop the kernel's launch stub)
+      const int q = i * 256 + tid, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
+      const int off = v_off<D, ESZ>(o + 16 * h, 16 * md + dl);
+      __builtin_amdgcn_global_load_lds(T.v + off, dst + (q >> 6) * 64, 16, 0, 0);
+    }
+  };
+  auto convert_fp8 = [&](int vk, int vv) {
     if (vk >= 0) {
+      const v4u* St = Sbase + (vk % NSTG) * (KST + VST);
       v4u* Ls = Kbase + (vk % NSLOT) * KSLOT;
 #pragma unroll
-      for (int i = 0; i < KLD; ++i) {
-        const int q = i * 256 + tid, lp = q & 63, fp = q >> 6;
-        const int mt = fp / (KS / 2), kq = fp % (KS / 2);
+      for (int i = 0; i < K8PW; ++i) {
+        const int fp = 4 * i + wave, mt = fp / (KS / 2), kq = fp % (KS / 2);
         const int f0 = mt * KS + 2 * kq;
-        Ls[f0 * 64 + lp] = __builtin_bit_cast(v4u, fp8x8_to_bf16(st_k[i][0], st_k[i][1]));
-        Ls[(f0 + 1) * 64 + lp] = __builtin_bit_cast(v4u, fp8x8_to_bf16(st_k[i][2], st_k[i][3]));
+        const v4u x = St[fp * 64 + lane];
+        Ls[f0 * 64 + lane] = __builtin_bit_cast(v4u, fp8x8_to_bf16(x[0], x[1]));
+        Ls[(f0 + 1) * 64 + lane] = __builtin_bit_cast(v4u, fp8x8_to_bf16(x[2], x[3]));
       }
     }
     if (vv >= 0) {
+      const v4u* St = Sbase + (vv % NSTG) * (KST + VST) + KST;
       v4u* Ls = Vbase + (vv % NSLOT) * VSLOT;
       const bool tail = vv * BK + BK > n_keys_t;
 #pragma unroll
-      for (int i = 0; i < VLD; ++i) {
-        const int q = i * 256 + tid, lp = q & 63;
-        v4u x = v4u{st_v[i][0], st_v[i][1], 0u, 0u};
-        if (tail) x = keep_first_b(x, n_keys_t - (vv * BK + 8 * (lp >> 4)));
-        Ls[q] = __builtin_bit_cast(v4u, fp8x8_to_bf16(x[0], x[1]));
+      for (int i = 0; i < V8PW; ++i) {
+        const int q = i * 256 + tid, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
+        v4u x = St[q];
+        if (tail) x = keep_first_b(x, n_keys_t - (vv * BK + 16 * h));
+        Ls[md * 64 + 32 * h + dl] = __builtin_bit_cast(v4u, fp8x8_to_bf16(x[0], x[1]));
+        Ls[md * 64 + 32 * h + 16 + dl] = __builtin_bit_cast(v4u, fp8x8_to_bf16(x[2], x[3]));
       }
     }
   };
@@ -378,14 +406,12 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   // then wait for the next step's tiles and release this step's slots.
   auto step = [&](int v, v4f (&Sc)[MT][NT], v4f (&Sn)[MT][NT]) {
     int issued = 0;
-    int vk = -1, vv = -1;
     if (KV == 0) {
-      if (v + 2 < n_st) { dma_v(v + 2); issued = 1; }
-      if (v + 3 < n_st) { dma_k(v + 3); issued = 2; }
+      if (v + 2 < v_hi) { dma_v(v + 2); issued = 1; }
+      if (v + 3 < v_hi) { dma_k(v + 3); issued = 2; }
     } else {
-      vk = v + 2 < n_st ? v + 2 : -1;
-      vv = v + 1 < n_st ? v + 1 : -1;
-      issue_fp8(vk, vv);
+      if (v + 4 < v_hi) dma8_k(v + 4);
+      if (v + 3 < v_hi) dma8_v(v + 3);
     }
     if (wave_active) {
       if (v * BK + BK - 1 > pos_first) mask(v, Sc);
@@ -409,49 +435,67 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       else if (issued == 1) wait_vmem<VPW>();
       else wait_vmem<0>();
     } else {
-      commit_fp8(vk, vv);
+      // K(v+2) and V(v+1) have landed once at most the DMAs issued in steps
+      // v-1 and v (K(v+3), V(v+2), K(v+4), V(v+3), those that exist) remain.
+      const int r = v_hi - 1 - v;
+      if (r >= 4) wait_vmem<2 * (K8PW + V8PW)>();
+      else if (r == 3) wait_vmem<K8PW + 2 * V8PW>();
+      else if (r == 2) wait_vmem<V8PW>();
+      else wait_vmem<0>();
+      convert_fp8(v + 2 < v_hi ? v + 2 : -1, v + 1 < v_hi ? v + 1 : -1);
     }
     lds_barrier();
-    if (KV == 0 && v + 1 < n_st && (v + 1) * BK + BK > n_keys_t) {
+    if (KV == 0 && v + 1 < v_hi && (v + 1) * BK + BK > n_keys_t) {
       zero_tail_bf16(v + 1);
       lds_barrier();
     }
   };
 
-  // Prologue: K(0), V(0), K(1) resident (bf16 also has K(2), V(1) in
-  // flight); S(0) computed; then the slot of K(0) may be reused.
-  v4f S0[MT][NT], S1[MT][NT];
-  if (KV == 0) {
-    dma_k(0);
-    dma_v(0);
-    if (n_st > 1) dma_k(1);
-    if (n_st > 1) dma_v(1);
-    if (n_st > 2) dma_k(2);
-    if (n_st > 2) wait_vmem<KPW + VPW>();
-    else if (n_st > 1) wait_vmem<VPW>();
-    else wait_vmem<0>();
-  } else {
-    issue_fp8(0, 0);
-    commit_fp8(0, 0);
-    if (n_st > 1) {
-      issue_fp8(1, -1);
-      commit_fp8(1, -1);
+  // Prologue: K(v_lo), V(v_lo), K(v_lo+1) resident as bf16 (bf16 also has
+  // K(v_lo+2), V(v_lo+1) in flight; fp8 has the codes of V(v_lo+1..v_lo+2)
+  // and K(v_lo+2..v_lo+3) in flight); S(v_lo) computed; then the slot of
+  // K(v_lo) may be reused.  A work item with no keys skips to its output.
+  if (v_hi > v_lo) {
+    const int n_st = v_hi - v_lo;
+    v4f S0[MT][NT], S1[MT][NT];
+    if (KV == 0) {
+      dma_k(v_lo);
+      dma_v(v_lo);
+      if (n_st > 1) dma_k(v_lo + 1);
+      if (n_st > 1) dma_v(v_lo + 1);
+      if (n_st > 2) dma_k(v_lo + 2);
+      if (n_st > 2) wait_vmem<KPW + VPW>();
+      else if (n_st > 1) wait_vmem<VPW>();
+      else wait_vmem<0>();
+    } else {
+      dma8_k(v_lo);
+      dma8_v(v_lo);
+      if (n_st > 1) dma8_k(v_lo + 1);
+      wait_vmem<0>();
+      convert_fp8(v_lo, v_lo);
+      if (n_st > 1) convert_fp8(v_lo + 1, -1);
+      // the staging reads above finish before K(v_lo+3) reuses K(v_lo)'s entries
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (n_st > 1) dma8_v(v_lo + 1);
+      if (n_st > 2) dma8_k(v_lo + 2);
+      if (n_st > 2) dma8_v(v_lo + 2);
+      if (n_st > 3) dma8_k(v_lo + 3);
     }
-  }
-  __syncthreads();
-  if (KV == 0 && BK > n_keys_t) {
-    zero_tail_bf16(0);
     __syncthreads();
-  }
-  if (wave_active) qk(0, S0);  // slot 0 holds K(0)
-  __syncthreads();
+    if (KV == 0 && v_lo * BK + BK > n_keys_t) {
+      zero_tail_bf16(v_lo);
+      __syncthreads();
+    }
+    if (wave_active) qk((v_lo % NSLOT) * KSLOT, S0);
+    __syncthreads();
 
-  for (int v = 0; v < n_st; ++v) {
-    step(v, S0, S1);
+    for (int v = v_lo; v < v_hi; ++v) {
+      step(v, S0, S1);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S0[mt][nt] = S1[mt][nt];
+        for (int nt = 0; nt < NT; ++nt) S0[mt][nt] = S1[mt][nt];
+    }
   }
 
   if (!wave_active) return;
@@ -460,8 +504,25 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
     float l = l_run[nt];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    const float f = bad ? __builtin_nanf("") : A.v_scale / l;
     if (!cok[nt]) continue;
+    if (split_mode) {
+      // Partial of (row, head, split): p was exp2(s*c - m_run*c), so the
+      // split's m in log2 units is exactly m_run*c; o stays in stored-V units.
+      const int64_t slot =
+          S.slot_base + ((int64_t)crow[nt] * A.n_q_heads + chead[nt]) * S.n_splits + split;
+      // A rejected page id poisons m as a NaN bit pattern (this file is built
+      // without NaN semantics, so no floating-point NaN is ever formed here).
+      if (a == 0) {
+        const uint32_t mb = bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, m_run[nt] * c);
+        reinterpret_cast<uint32_t*>(A.ws_ml)[2 * slot] = mb;
+        A.ws_ml[2 * slot + 1] = l;
+      }
+      float* dst = A.ws_o + slot * D + 4 * a;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) *reinterpret_cast<v4f*>(dst + 16 * md) = o[md][nt];
+      continue;
+    }
+    const float f = A.v_scale / l;
     uint16_t* dst =
         A.out + ((int64_t)(S.row_offset + crow[nt]) * A.n_q_heads + chead[nt]) * D + 4 * a;
 #pragma unroll
@@ -470,6 +531,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       v2u w;
       w[0] = pack_bf2(x[0], x[1]);
       w[1] = pack_bf2(x[2], x[3]);
+      if (bad) w = v2u{0x7FC07FC0u, 0x7FC07FC0u};  // bf16 NaN bits for a rejected page id
       *reinterpret_cast<v2u*>(dst + 16 * md) = w;
     }
   }

@@ -37,6 +37,15 @@ def test_library_exports_every_declared_symbol():
     assert pa.lib().pa_version() >> 16 == 1
 
 
+def test_every_kernel_launch_stub_is_defined():
+    """Each kernel's host-side launch stub is defined in the library (a stub
+    the host pass failed to emit would only show as a load error)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", pa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert "__device_stub__" not in out, out
+
+
 def test_status_strings():
     for code in range(0, -8, -1):
         assert pa.status_string(code) and pa.status_string(code) != "unknown status"
@@ -181,8 +190,27 @@ def test_decode_plan_verify_rows_and_ragged_lengths():
         off += 16
     splits, plan = _plan(ss)
     assert list(splits) == [math.ceil(L / 4096) for L in lens]
-    assert plan.col_tiles == math.ceil(6 * 16 / 16)
-    assert plan.partial_blocks == sum(splits) * 6 * 4
+    # 16 rows x 6 q heads = 96 columns per kv head: one row-tile workgroup
+    # per (split, kv head) covers them all; the streaming kernel runs none
+    assert plan.col_tiles == 0
+    assert plan.partial_blocks == plan.wide_blocks == sum(splits) * 4
+
+
+def test_decode_plan_kernel_choice_per_stream():
+    # up to 32 (row, head) columns per kv head stream through registers
+    # (one 16-column tile per workgroup); wider streams share LDS tiles
+    ss = [stream(ctx_len=8192, n_rows=5, first_pos=8187, row_offset=0),
+          stream(ctx_len=8192, n_rows=6, first_pos=8186, row_offset=5)]
+    splits, plan = _plan(ss)
+    assert list(splits) == [2, 2]
+    assert plan.col_tiles == 2  # 30 columns
+    assert plan.wide_blocks == 2 * 4
+    assert plan.partial_blocks == 2 * 2 * 4 + 2 * 4
+    # head_dim 128: 48 columns a wave, 192 a workgroup; a group of 16 with
+    # 16 rows (256 columns) needs two row tiles of 12 rows
+    ss = [stream(ctx_len=4096, n_rows=16, first_pos=4080)]
+    _, plan = pa.paged_attn_decode_plan(ss, 32, 2, 128, 4096)
+    assert plan.wide_blocks == plan.partial_blocks == 2 * 2
 
 
 def test_decode_plan_per_stream_independent_of_batch():
