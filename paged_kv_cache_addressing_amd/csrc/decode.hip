@@ -147,8 +147,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(const DecodeArgs
           sv[mt][i] = v;
           mx = fmaxf(mx, v);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = rows4_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -198,8 +197,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(const DecodeArgs
   }
 
   // Per-column row sum across the four lane groups, in a fixed order.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = rows4_sum(l_run);
 
   if (wave > 0) {
 #pragma unroll

@@ -56,6 +56,30 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2bf));
 }
 
+// Reductions over the four 16-lane rows of a wave (the four lane groups that
+// hold the C rows of one MFMA column), the result in every row.  Two lane
+// swaps (v_permlane16_swap: rows 0<->1 and 2<->3; v_permlane32_swap: the two
+// halves) keep them off the LDS.  Both operand orders give the same bits, so
+// every row gets the identical value.
+__device__ __forceinline__ float rows4_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m = fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]),
+                        __builtin_bit_cast(float, (uint32_t)p[1]));
+  const uint32_t w = __builtin_bit_cast(uint32_t, m);
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)q[0]), __builtin_bit_cast(float, (uint32_t)q[1]));
+}
+
+__device__ __forceinline__ float rows4_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m = __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+  const uint32_t w = __builtin_bit_cast(uint32_t, m);
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __builtin_bit_cast(float, (uint32_t)q[0]) + __builtin_bit_cast(float, (uint32_t)q[1]);
+}
+
 // Keep the first `nv` 16-bit elements of an 8 x bf16 vector, zero the rest.
 __device__ __forceinline__ v4u keep_first_h(v4u x, int nv) {
 #pragma unroll

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   // the constant fragment offsets away from the ds_read immediate field.
   auto lane_base = [&](lds_v4u* slot0, int slot) -> const lds_v4u* {
     uint32_t addr = (uint32_t)(uintptr_t)(slot0 + slot + lane);
-    asm volatile("" : "+v"(addr));
+    asm("" : "+v"(addr));
     return (const lds_v4u*)(uintptr_t)addr;
   };
   // The K loader runs ahead of the V loader; each keeps its own page, so
@@ -352,8 +352,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
     for (int nt = 0; nt < NT; ++nt) {
       float mx = fmaxf(fmaxf(fmaxf(Sx[0][nt][0], Sx[0][nt][1]), fmaxf(Sx[0][nt][2], Sx[0][nt][3])),
                        fmaxf(fmaxf(Sx[1][nt][0], Sx[1][nt][1]), fmaxf(Sx[1][nt][2], Sx[1][nt][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = rows4_max(mx);
       float mu = m_run[nt];
       if (mx > mu + thr) mu = mx;
       alpha[nt] = mu == m_run[nt] ? 1.f : __builtin_amdgcn_exp2f((m_run[nt] - mu) * c);
@@ -376,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       x[3] = pack_bf2(Sx[1][nt][2], Sx[1][nt][3]);
       // Materialise P here, beside the QK MFMAs, rather than letting it sink
       // next to the P.V MFMAs that depend on it.
-      asm volatile("" : "+v"(x));
+      asm("" : "+v"(x));
       P[nt] = as_bf(x);
     }
   };
@@ -502,8 +501,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float l = l_run[nt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = rows4_sum(l);
     if (!cok[nt]) continue;
     if (split_mode) {
       // Partial of (row, head, split): p was exp2(s*c - m_run*c), so the
