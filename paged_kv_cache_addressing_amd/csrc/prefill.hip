@@ -44,6 +44,8 @@
 // masked for a row leaves its state bit-identical (max unchanged, alpha = 1,
 // p = 0 against finite or zeroed values).  So any slicing of a stream's rows
 // across calls gives the same bytes as one call.
+#include <type_traits>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
   const int n = lane & 15;
   const int a = lane >> 4;
   const int G = A.group;
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       __builtin_amdgcn_global_load_lds(T.v + off, dst + (q >> 6) * 64, 16, 0, 0);
     }
   };
-  auto convert_fp8 = [&](int vk, int vv) {
+  auto convert_fp8 = [&](int vk, int vv, auto may_tail) {
     if (vk >= 0) {
       const v4u* St = Sbase + (vk % NSTG) * (KST + VST);
       v4u* Ls = Kbase + (vk % NSLOT) * KSLOT;
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
     if (vv >= 0) {
       const v4u* St = Sbase + (vv % NSTG) * (KST + VST) + KST;
       v4u* Ls = Vbase + (vv % NSLOT) * VSLOT;
-      const bool tail = vv * BK + BK > n_keys_t;
+      const bool tail = decltype(may_tail)::value && vv * BK + BK > n_keys_t;
 #pragma unroll
       for (int i = 0; i < V8PW; ++i) {
         const int q = i * 256 + tid, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
@@ -303,39 +305,6 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   const float c = A.scale_log2;
   const float thr = 8.f / c;  // move the max only past p = 2^8
 
-  // The LDS reads of a product are issued in batches of FB fragments, the
-  // next batch in flight while the current one feeds the matrix cores, so
-  // LDS latency overlaps MFMA work instead of stalling before every MFMA.
-  constexpr int FB = 4;
-  auto qk = [&](int kslot, v4f (&Sx)[MT][NT]) {
-    const lds_v4u* Lk = lane_base(Kb3, kslot);  // fragment f at Lk[f * 64]
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) Sx[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-    // visit order j = ks * MT + mt; fragment index mt * KS + ks
-    v4u fb[2][FB];
-#pragma unroll
-    for (int j = 0; j < FB; ++j) fb[0][j] = Lk[((j % MT) * KS + j / MT) * 64];
-#pragma unroll
-    for (int b = 0; b < KF / FB; ++b) {
-      if (b + 1 < KF / FB) {
-#pragma unroll
-        for (int j = 0; j < FB; ++j) {
-          const int f = (b + 1) * FB + j;
-          fb[(b + 1) & 1][j] = Lk[((f % MT) * KS + f / MT) * 64];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < FB; ++j) {
-        const int f = b * FB + j, ks = f / MT, mt = f % MT;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          Sx[mt][nt] = mfma16(as_bf(fb[b & 1][j]), qb[nt][ks], Sx[mt][nt]);
-      }
-    }
-  };
-
   auto mask = [&](int v, v4f (&Sx)[MT][NT]) {
     const int kabs0 = v * BK + 8 * a;
 #pragma unroll
@@ -347,77 +316,138 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
           if (kabs0 + 4 * mt + i > cpos[nt]) Sx[mt][nt][i] = -INFINITY;
   };
 
-  auto softmax = [&](v4f (&Sx)[MT][NT], v8bf (&P)[NT], float (&alpha)[NT]) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = fmaxf(fmaxf(fmaxf(Sx[0][nt][0], Sx[0][nt][1]), fmaxf(Sx[0][nt][2], Sx[0][nt][3])),
-                       fmaxf(fmaxf(Sx[1][nt][0], Sx[1][nt][1]), fmaxf(Sx[1][nt][2], Sx[1][nt][3])));
-      mx = rows4_max(mx);
-      float mu = m_run[nt];
-      if (mx > mu + thr) mu = mx;
-      alpha[nt] = mu == m_run[nt] ? 1.f : __builtin_amdgcn_exp2f((m_run[nt] - mu) * c);
-      m_run[nt] = mu;
-      const float mc = mu == -INFINITY ? 0.f : mu * c;
-      float ps = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+  // S(v+1) = K(v+1) Q^T on the matrix cores with the softmax of S(v) on the
+  // VALU, in a fixed interleaved order.  With one wave per SIMD nothing else
+  // hides latency, so the order is pinned with sched_barrier: the K fragment
+  // reads run RA fragments ahead of their MFMAs (a ring of RA+1 registers),
+  // and the softmax is cut into 5*NT chunks spread between the MFMAs, where
+  // the VALU work issues while the matrix cores are busy.
+  //   chunk k <  NT      : row max over the lane's 8 logits of n-tile k
+  //   chunk k < 2NT      : the max over the column's four lane rows, the new
+  //                        running max (moved only past p = 2^8), alpha
+  //   chunk k < 2NT+MT*NT: p = exp2(s*c - m*c) for 4 logits, partial sums
+  //   else               : l update and the bf16 P^T operand
+  constexpr int RA = 4;                  // LDS reads in flight ahead of use
+  constexpr int NCH = 5 * NT;            // softmax chunks
+  auto qk_softmax = [&](int kslot, v4f (&Sn)[MT][NT], v4f (&Sc)[MT][NT], v8bf (&P)[NT],
+                        float (&alpha)[NT]) {
+    const lds_v4u* Lk = lane_base(Kb3, kslot);  // fragment f at Lk[f * 64]
+    float mx[NT], mc[NT], ps[NT];
+    auto chunk = [&](int k) {
+      if (k < NT) {
+        const int nt = k;
+        mx[nt] = fmaxf(fmaxf(fmaxf(Sc[0][nt][0], Sc[0][nt][1]), fmaxf(Sc[0][nt][2], Sc[0][nt][3])),
+                       fmaxf(fmaxf(Sc[1][nt][0], Sc[1][nt][1]), fmaxf(Sc[1][nt][2], Sc[1][nt][3])));
+      } else if (k < 2 * NT) {
+        const int nt = k - NT;
+        const float m = rows4_max(mx[nt]);
+        float mu = m_run[nt];
+        if (m > mu + thr) mu = m;
+        alpha[nt] = mu == m_run[nt] ? 1.f : __builtin_amdgcn_exp2f((m_run[nt] - mu) * c);
+        m_run[nt] = mu;
+        mc[nt] = mu == -INFINITY ? 0.f : mu * c;
+        ps[nt] = 0.f;
+      } else if (k < 2 * NT + MT * NT) {
+        const int nt = (k - 2 * NT) / MT, mt = (k - 2 * NT) % MT;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Sx[mt][nt][i], c, -mc));
-          Sx[mt][nt][i] = p;
-          ps += p;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[mt][nt][i], c, -mc[nt]));
+          Sc[mt][nt][i] = p;
+          ps[nt] += p;
         }
-      l_run[nt] = l_run[nt] * alpha[nt] + ps;
-      v4u x;
-      x[0] = pack_bf2(Sx[0][nt][0], Sx[0][nt][1]);
-      x[1] = pack_bf2(Sx[0][nt][2], Sx[0][nt][3]);
-      x[2] = pack_bf2(Sx[1][nt][0], Sx[1][nt][1]);
-      x[3] = pack_bf2(Sx[1][nt][2], Sx[1][nt][3]);
-      // Materialise P here, beside the QK MFMAs, rather than letting it sink
-      // next to the P.V MFMAs that depend on it.
-      asm("" : "+v"(x));
-      P[nt] = as_bf(x);
+      } else {
+        const int nt = k - 2 * NT - MT * NT;
+        l_run[nt] = l_run[nt] * alpha[nt] + ps[nt];
+        v4u x;
+        x[0] = pack_bf2(Sc[0][nt][0], Sc[0][nt][1]);
+        x[1] = pack_bf2(Sc[0][nt][2], Sc[0][nt][3]);
+        x[2] = pack_bf2(Sc[1][nt][0], Sc[1][nt][1]);
+        x[3] = pack_bf2(Sc[1][nt][2], Sc[1][nt][3]);
+        // keep P here: otherwise the exponentials sink past the rescale
+        // branch, next to the P.V products that consume them
+        asm volatile("" : "+v"(x));
+        P[nt] = as_bf(x);
+      }
+    };
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) Sn[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+    // visit order j = ks * MT + mt reads fragment mt * KS + ks
+    v4u fb[RA + 1];
+#pragma unroll
+    for (int j = 0; j < RA; ++j) fb[j] = Lk[((j % MT) * KS + j / MT) * 64];
+#pragma unroll
+    for (int j = 0; j < KF; ++j) {
+      if (j + RA < KF) {
+        const int f = j + RA;
+        fb[f % (RA + 1)] = Lk[((f % MT) * KS + f / MT) * 64];
+      }
+      const int ks = j / MT, mt = j % MT;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        Sn[mt][nt] = mfma16(as_bf(fb[j % (RA + 1)]), qb[nt][ks], Sn[mt][nt]);
+      // softmax chunks placed after this fragment: k with slot(k) == j
+#pragma unroll
+      for (int k = 0; k < NCH; ++k)
+        if ((k + 1) * KF / (NCH + 1) == j) chunk(k);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // O^T += V(v)^T P^T: 16-dim V fragments read RA ahead of their MFMAs.
   auto pv = [&](int vslot, v8bf (&P)[NT]) {
     const lds_v4u* Lv = lane_base(Vb3, vslot);  // fragment md at Lv[md * 64]
-    v4u fb[2][FB];
+    v4u fb[RA + 1];
 #pragma unroll
-    for (int j = 0; j < FB; ++j) fb[0][j] = Lv[j * 64];
+    for (int j = 0; j < RA; ++j) fb[j] = Lv[j * 64];
 #pragma unroll
-    for (int b = 0; b < VF / FB; ++b) {
-      if (b + 1 < VF / FB) {
+    for (int md = 0; md < VF; ++md) {
+      if (md + RA < VF) fb[(md + RA) % (RA + 1)] = Lv[(md + RA) * 64];
 #pragma unroll
-        for (int j = 0; j < FB; ++j) fb[(b + 1) & 1][j] = Lv[((b + 1) * FB + j) * 64];
-      }
+      for (int nt = 0; nt < NT; ++nt)
+        o[md][nt] = mfma16(as_bf(fb[md % (RA + 1)]), P[nt], o[md][nt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Prologue helper: S(v_lo) alone (no softmax to overlap yet).
+  auto qk = [&](int kslot, v4f (&Sx)[MT][NT]) {
+    const lds_v4u* Lk = lane_base(Kb3, kslot);
 #pragma unroll
-      for (int j = 0; j < FB; ++j) {
-        const int md = b * FB + j;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[md][nt] = mfma16(as_bf(fb[b & 1][j]), P[nt], o[md][nt]);
-      }
+      for (int nt = 0; nt < NT; ++nt) Sx[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int f = 0; f < KF; ++f) {
+      const int mt = f / KS, ks = f % KS;
+      const v4u kf = Lk[f * 64];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) Sx[mt][nt] = mfma16(as_bf(kf), qb[nt][ks], Sx[mt][nt]);
     }
   };
 
   // One step: issue the loads two (bf16) or one (fp8) steps ahead; S(v+1)
   // on the matrix cores alongside softmax(v) on the VALU; O += V(v) P(v);
   // then wait for the next step's tiles and release this step's slots.
-  auto step = [&](int v, v4f (&Sc)[MT][NT], v4f (&Sn)[MT][NT]) {
+  // FAST is the steady state (every prefetch in range, no causal mask, no
+  // key-range tail), where the step runs without any of those checks.
+  auto step = [&](int v, v4f (&Sc)[MT][NT], v4f (&Sn)[MT][NT], auto fast) {
+    constexpr bool FAST = decltype(fast)::value;
     int issued = 0;
     if (KV == 0) {
-      if (v + 2 < v_hi) { dma_v(v + 2); issued = 1; }
-      if (v + 3 < v_hi) { dma_k(v + 3); issued = 2; }
+      if (FAST || v + 2 < v_hi) { dma_v(v + 2); issued = 1; }
+      if (FAST || v + 3 < v_hi) { dma_k(v + 3); issued = 2; }
     } else {
-      if (v + 4 < v_hi) dma8_k(v + 4);
-      if (v + 3 < v_hi) dma8_v(v + 3);
+      if (FAST || v + 4 < v_hi) dma8_k(v + 4);
+      if (FAST || v + 3 < v_hi) dma8_v(v + 3);
     }
     if (wave_active) {
-      if (v * BK + BK - 1 > pos_first) mask(v, Sc);
+      if (!FAST && v * BK + BK - 1 > pos_first) mask(v, Sc);
       v8bf P[NT];
       float alpha[NT];
-      qk(((v + 1) % NSLOT) * KSLOT, Sn);  // K(v+1), or stale data past the end (unused)
-      softmax(Sc, P, alpha);
+      // K(v+1), or stale data past the end (unused)
+      qk_softmax(((v + 1) % NSLOT) * KSLOT, Sn, Sc, P, alpha);
       bool moved = false;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) moved |= alpha[nt] != 1.f;
@@ -430,21 +460,22 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       pv((v % NSLOT) * VSLOT, P);
     }
     if (KV == 0) {
-      if (issued == 2) wait_vmem<KPW + VPW>();
+      if (FAST || issued == 2) wait_vmem<KPW + VPW>();
       else if (issued == 1) wait_vmem<VPW>();
       else wait_vmem<0>();
     } else {
       // K(v+2) and V(v+1) have landed once at most the DMAs issued in steps
       // v-1 and v (K(v+3), V(v+2), K(v+4), V(v+3), those that exist) remain.
       const int r = v_hi - 1 - v;
-      if (r >= 4) wait_vmem<2 * (K8PW + V8PW)>();
+      if (FAST || r >= 4) wait_vmem<2 * (K8PW + V8PW)>();
       else if (r == 3) wait_vmem<K8PW + 2 * V8PW>();
       else if (r == 2) wait_vmem<V8PW>();
       else wait_vmem<0>();
-      convert_fp8(v + 2 < v_hi ? v + 2 : -1, v + 1 < v_hi ? v + 1 : -1);
+      if (FAST) convert_fp8(v + 2, v + 1, std::false_type{});
+      else convert_fp8(v + 2 < v_hi ? v + 2 : -1, v + 1 < v_hi ? v + 1 : -1, std::true_type{});
     }
     lds_barrier();
-    if (KV == 0 && v + 1 < v_hi && (v + 1) * BK + BK > n_keys_t) {
+    if (!FAST && KV == 0 && v + 1 < v_hi && (v + 1) * BK + BK > n_keys_t) {
       zero_tail_bf16(v + 1);
       lds_barrier();
     }
@@ -471,8 +502,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       dma8_v(v_lo);
       if (n_st > 1) dma8_k(v_lo + 1);
       wait_vmem<0>();
-      convert_fp8(v_lo, v_lo);
-      if (n_st > 1) convert_fp8(v_lo + 1, -1);
+      convert_fp8(v_lo, v_lo, std::true_type{});
+      if (n_st > 1) convert_fp8(v_lo + 1, -1, std::true_type{});
       // the staging reads above finish before K(v_lo+3) reuses K(v_lo)'s entries
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (n_st > 1) dma8_v(v_lo + 1);
@@ -488,8 +519,21 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
     if (wave_active) qk((v_lo % NSLOT) * KSLOT, S0);
     __syncthreads();
 
-    for (int v = v_lo; v < v_hi; ++v) {
-      step(v, S0, S1);
+    // Steps [v_lo, v_fast) are steady state: v+3 (bf16) or v+4 (fp8) is
+    // still in range, no key of the step is past the first row's position,
+    // and the next V step holds no key at or past n_keys_t.
+    const int v_fast = max(v_lo, min(min(v_hi - (KV ? 4 : 3), (pos_first + 1) / BK),
+                                     n_keys_t / BK - 1));
+    int v = v_lo;
+    for (; v < v_fast; ++v) {
+      step(v, S0, S1, std::true_type{});
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) S0[mt][nt] = S1[mt][nt];
+    }
+    for (; v < v_hi; ++v) {
+      step(v, S0, S1, std::false_type{});
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
