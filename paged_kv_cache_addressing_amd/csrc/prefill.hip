@@ -200,10 +200,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   // Each DMA is the step's base in the page tile (o*D*2 bytes for both K
   // and V: wave-uniform, SGPRs) plus a per-lane offset that does not depend
   // on the step (loop invariant, hoisted into VGPRs).
-  auto dma_k = [&](int v) {
+  auto dma_k = [&](int v, int sl) {
     const PageTile& T = page_k(v);
     const uint8_t* base = T.k + (int64_t)(v & 7) * BK * D * 2;
-    v4u* dst = Kbase + (v % NSLOT) * KSLOT + wave * KPW * 64;
+    v4u* dst = Kbase + sl * KSLOT + wave * KPW * 64;
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
       const int f = wave * KPW + i, mt = f / KS, ks = f % KS;
@@ -211,10 +211,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       __builtin_amdgcn_global_load_lds(base + off, dst + i * 64, 16, 0, 0);
     }
   };
-  auto dma_v = [&](int v) {
+  auto dma_v = [&](int v, int sl) {
     const PageTile& T = page_v(v);
     const uint8_t* base = T.v + (int64_t)(v & 7) * BK * D * 2;
-    v4u* dst = Vbase + (v % NSLOT) * VSLOT + wave * VPW * 64;
+    v4u* dst = Vbase + sl * VSLOT + wave * VPW * 64;
 #pragma unroll
     for (int i = 0; i < VPW; ++i) {
       const int off = v_off<D, ESZ>(8 * a, 16 * (wave * VPW + i) + n) * 2;
@@ -222,8 +222,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
     }
   };
   // bf16 tail: values at or past n_keys_t in a landed V step become zeros.
-  auto zero_tail_bf16 = [&](int v) {
-    v4u* Ls = Vbase + (v % NSLOT) * VSLOT;
+  auto zero_tail_bf16 = [&](int v, int sl) {
+    v4u* Ls = Vbase + sl * VSLOT;
 #pragma unroll
     for (int i = 0; i < VSLOT / 256; ++i) {
       const int q = i * 256 + tid, lp = q & 63;
@@ -237,10 +237,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   // ahead of use (K two steps).  Every E4M3FN value is a bf16 value, so the
   // conversion is exact.
   v4u* const Sbase = lds + NSLOT * (KSLOT + VSLOT);
-  auto dma8_k = [&](int v) {
+  auto dma8_k = [&](int v, int sl) {
     const PageTile& T = page_k(v);
     const uint8_t* base = T.k + (int64_t)(v & 7) * BK * D;
-    v4u* dst = Sbase + (v % NSTG) * (KST + VST);
+    v4u* dst = Sbase + sl * (KST + VST);
 #pragma unroll
     for (int i = 0; i < K8PW; ++i) {
       // entry fp*64 + lane: 16 dims (two QK k-steps) of one S^T row
@@ -249,10 +249,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       __builtin_amdgcn_global_load_lds(base + off, dst + fp * 64, 16, 0, 0);
     }
   };
-  auto dma8_v = [&](int v) {
+  auto dma8_v = [&](int v, int sl) {
     const PageTile& T = page_v(v);
     const int o = (v & 7) * BK;
-    v4u* dst = Sbase + (v % NSTG) * (KST + VST) + KST;
+    v4u* dst = Sbase + sl * (KST + VST) + KST;
 #pragma unroll
     for (int i = 0; i < V8PW; ++i) {
       // entry q: 16 keys (half h of the step) of dim 16*md + dl
@@ -263,10 +263,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       __builtin_amdgcn_global_load_lds(T.v + off, dst + (q >> 6) * 64, 16, 0, 0);
     }
   };
-  auto convert_fp8 = [&](int vk, int vv, auto may_tail) {
+  auto convert_fp8 = [&](int vk, int slk, int vv, int slv, auto may_tail) {
     if (vk >= 0) {
-      const v4u* St = Sbase + (vk % NSTG) * (KST + VST);
-      v4u* Ls = Kbase + (vk % NSLOT) * KSLOT;
+      const v4u* St = Sbase + slk * (KST + VST);
+      v4u* Ls = Kbase + slk * KSLOT;
 #pragma unroll
       for (int i = 0; i < K8PW; ++i) {
         const int fp = 4 * i + wave, mt = fp / (KS / 2), kq = fp % (KS / 2);
@@ -277,8 +277,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       }
     }
     if (vv >= 0) {
-      const v4u* St = Sbase + (vv % NSTG) * (KST + VST) + KST;
-      v4u* Ls = Vbase + (vv % NSLOT) * VSLOT;
+      const v4u* St = Sbase + slv * (KST + VST) + KST;
+      v4u* Ls = Vbase + slv * VSLOT;
       const bool tail = decltype(may_tail)::value && vv * BK + BK > n_keys_t;
 #pragma unroll
       for (int i = 0; i < V8PW; ++i) {
@@ -431,23 +431,28 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   // on the matrix cores alongside softmax(v) on the VALU; O += V(v) P(v);
   // then wait for the next step's tiles and release this step's slots.
   // FAST is the steady state (every prefetch in range, no causal mask, no
-  // key-range tail), where the step runs without any of those checks.
-  auto step = [&](int v, v4f (&Sc)[MT][NT], v4f (&Sn)[MT][NT], auto fast) {
+  // key-range tail), where the step runs without any of those checks.  LDS
+  // slots (and fp8 staging entries) rotate with the step: step v uses ring
+  // position (v - v_lo) % 3, passed in as `ph` (a compile-time constant in
+  // the unrolled steady state).
+  static_assert(NSLOT == 3 && NSTG == 3, "one ring period for slots and staging");
+  auto step = [&](int v, v4f (&Sc)[MT][NT], v4f (&Sn)[MT][NT], auto fast, auto ph) {
     constexpr bool FAST = decltype(fast)::value;
+    const int r0 = ph % 3, r1 = (ph + 1) % 3, r2 = (ph + 2) % 3;  // v, v+1 (and v+4), v+2
     int issued = 0;
     if (KV == 0) {
-      if (FAST || v + 2 < v_hi) { dma_v(v + 2); issued = 1; }
-      if (FAST || v + 3 < v_hi) { dma_k(v + 3); issued = 2; }
+      if (FAST || v + 2 < v_hi) { dma_v(v + 2, r2); issued = 1; }
+      if (FAST || v + 3 < v_hi) { dma_k(v + 3, r0); issued = 2; }
     } else {
-      if (FAST || v + 4 < v_hi) dma8_k(v + 4);
-      if (FAST || v + 3 < v_hi) dma8_v(v + 3);
+      if (FAST || v + 4 < v_hi) dma8_k(v + 4, r1);
+      if (FAST || v + 3 < v_hi) dma8_v(v + 3, r0);
     }
     if (wave_active) {
       if (!FAST && v * BK + BK - 1 > pos_first) mask(v, Sc);
       v8bf P[NT];
       float alpha[NT];
       // K(v+1), or stale data past the end (unused)
-      qk_softmax(((v + 1) % NSLOT) * KSLOT, Sn, Sc, P, alpha);
+      qk_softmax(r1 * KSLOT, Sn, Sc, P, alpha);
       bool moved = false;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) moved |= alpha[nt] != 1.f;
@@ -457,7 +462,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) o[md][nt] *= alpha[nt];
       }
-      pv((v % NSLOT) * VSLOT, P);
+      pv(r0 * VSLOT, P);
     }
     if (KV == 0) {
       if (FAST || issued == 2) wait_vmem<KPW + VPW>();
@@ -471,12 +476,13 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       else if (r == 3) wait_vmem<K8PW + 2 * V8PW>();
       else if (r == 2) wait_vmem<V8PW>();
       else wait_vmem<0>();
-      if (FAST) convert_fp8(v + 2, v + 1, std::false_type{});
-      else convert_fp8(v + 2 < v_hi ? v + 2 : -1, v + 1 < v_hi ? v + 1 : -1, std::true_type{});
+      if (FAST) convert_fp8(v + 2, r2, v + 1, r1, std::false_type{});
+      else convert_fp8(v + 2 < v_hi ? v + 2 : -1, r2, v + 1 < v_hi ? v + 1 : -1, r1,
+                       std::true_type{});
     }
     lds_barrier();
     if (!FAST && KV == 0 && v + 1 < v_hi && (v + 1) * BK + BK > n_keys_t) {
-      zero_tail_bf16(v + 1);
+      zero_tail_bf16(v + 1, r1);
       lds_barrier();
     }
   };
@@ -489,34 +495,34 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
     const int n_st = v_hi - v_lo;
     v4f S0[MT][NT], S1[MT][NT];
     if (KV == 0) {
-      dma_k(v_lo);
-      dma_v(v_lo);
-      if (n_st > 1) dma_k(v_lo + 1);
-      if (n_st > 1) dma_v(v_lo + 1);
-      if (n_st > 2) dma_k(v_lo + 2);
+      dma_k(v_lo, 0);
+      dma_v(v_lo, 0);
+      if (n_st > 1) dma_k(v_lo + 1, 1);
+      if (n_st > 1) dma_v(v_lo + 1, 1);
+      if (n_st > 2) dma_k(v_lo + 2, 2);
       if (n_st > 2) wait_vmem<KPW + VPW>();
       else if (n_st > 1) wait_vmem<VPW>();
       else wait_vmem<0>();
     } else {
-      dma8_k(v_lo);
-      dma8_v(v_lo);
-      if (n_st > 1) dma8_k(v_lo + 1);
+      dma8_k(v_lo, 0);
+      dma8_v(v_lo, 0);
+      if (n_st > 1) dma8_k(v_lo + 1, 1);
       wait_vmem<0>();
-      convert_fp8(v_lo, v_lo, std::true_type{});
-      if (n_st > 1) convert_fp8(v_lo + 1, -1, std::true_type{});
+      convert_fp8(v_lo, 0, v_lo, 0, std::true_type{});
+      if (n_st > 1) convert_fp8(v_lo + 1, 1, -1, 0, std::true_type{});
       // the staging reads above finish before K(v_lo+3) reuses K(v_lo)'s entries
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (n_st > 1) dma8_v(v_lo + 1);
-      if (n_st > 2) dma8_k(v_lo + 2);
-      if (n_st > 2) dma8_v(v_lo + 2);
-      if (n_st > 3) dma8_k(v_lo + 3);
+      if (n_st > 1) dma8_v(v_lo + 1, 1);
+      if (n_st > 2) dma8_k(v_lo + 2, 2);
+      if (n_st > 2) dma8_v(v_lo + 2, 2);
+      if (n_st > 3) dma8_k(v_lo + 3, 0);
     }
     __syncthreads();
     if (KV == 0 && v_lo * BK + BK > n_keys_t) {
-      zero_tail_bf16(v_lo);
+      zero_tail_bf16(v_lo, 0);
       __syncthreads();
     }
-    if (wave_active) qk((v_lo % NSLOT) * KSLOT, S0);
+    if (wave_active) qk(0, S0);
     __syncthreads();
 
     // Steps [v_lo, v_fast) are steady state: v+3 (bf16) or v+4 (fp8) is
@@ -524,20 +530,28 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
     // and the next V step holds no key at or past n_keys_t.
     const int v_fast = max(v_lo, min(min(v_hi - (KV ? 4 : 3), (pos_first + 1) / BK),
                                      n_keys_t / BK - 1));
-    int v = v_lo;
-    for (; v < v_fast; ++v) {
-      step(v, S0, S1, std::true_type{});
+    // The steady state runs three steps per iteration, one per ring
+    // position, so every slot address is a constant; S(v+1) alternates
+    // between S0 and S1.
+    auto copy_s = [&](v4f (&dst)[MT][NT], v4f (&src)[MT][NT]) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) S0[mt][nt] = S1[mt][nt];
+        for (int nt = 0; nt < NT; ++nt) dst[mt][nt] = src[mt][nt];
+    };
+    typedef std::integral_constant<int, 0> P0;
+    typedef std::integral_constant<int, 1> P1;
+    typedef std::integral_constant<int, 2> P2;
+    int v = v_lo;
+    for (; v + 3 <= v_fast; v += 3) {
+      step(v, S0, S1, std::true_type{}, P0{});
+      step(v + 1, S1, S0, std::true_type{}, P1{});
+      step(v + 2, S0, S1, std::true_type{}, P2{});
+      copy_s(S0, S1);
     }
     for (; v < v_hi; ++v) {
-      step(v, S0, S1, std::false_type{});
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) S0[mt][nt] = S1[mt][nt];
+      step(v, S0, S1, std::false_type{}, (v - v_lo) % 3);
+      copy_s(S0, S1);
     }
   }
 
