@@ -147,8 +147,8 @@ size_t ws_bytes(int64_t total_slots, int32_t head_dim) {
 }
 
 // Row tiling of the row-tile kernel: a workgroup covers `heads` q heads of
-// one kv head (a divisor of the group) and `rows` rows, its 4 waves holding
-// 4 * columns-per-wave (row, head) columns.
+// one kv head (a divisor of the group) and `rows` rows, its waves holding
+// prefill_wg_columns (row, head) columns.
 struct RowTiling {
   int32_t heads;
   int32_t rows;
@@ -162,14 +162,14 @@ RowTiling prefill_tiling(int32_t head_dim, int32_t group) {
   int32_t hw = 1;
   for (int32_t d = 1; d <= group && d <= cols; ++d)
     if (group % d == 0 && cols % d == 0) hw = d;
-  return {hw, 4 * cols / hw};
+  return {hw, pa::prefill_wg_columns(head_dim) / hw};
 }
 
 // Decode streams with many columns: the largest divisor of the group that
 // fits the workgroup's columns (the whole group whenever it fits), so every
 // split's K/V is read by as few workgroups as possible.
 RowTiling wide_tiling(int32_t head_dim, int32_t group) {
-  const int32_t cols = 4 * pa::prefill_columns(head_dim);
+  const int32_t cols = pa::prefill_wg_columns(head_dim);
   int32_t hw = 1;
   for (int32_t d = 1; d <= group && d <= cols; ++d)
     if (group % d == 0) hw = d;

@@ -13,6 +13,8 @@ int launch_decode_partials(const DecodeArgs& A, int kv_dtype, int head_dim, int 
 int launch_decode_merge(const DecodeArgs& A, int head_dim, hipStream_t st);
 // MFMA columns ((row, q head) pairs) one prefill wave covers at head_dim.
 int prefill_columns(int head_dim);
+// MFMA columns one row-tile workgroup covers (all its waves) at head_dim.
+int prefill_wg_columns(int head_dim);
 int launch_prefill(const PrefillArgs& A, int kv_dtype, int head_dim, hipStream_t st);
 int launch_write_kv(const WriteArgs& A, int kv_dtype, int head_dim, hipStream_t st);
 

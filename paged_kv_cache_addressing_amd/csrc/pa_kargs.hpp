@@ -10,9 +10,13 @@ namespace pa {
 constexpr int kPage = 256;            // positions per page (compile-time everywhere)
 constexpr int kMaxLaunchStreams = 32; // streams per kernel launch; calls are chunked
 
-// 16-column MFMA n-tiles per prefill wave: 3 (48 columns) where the O^T
-// accumulators fit beside Q^T and two S tiles, 2 (32 columns) at head_dim 256.
-constexpr int prefill_ntiles(int head_dim) { return head_dim >= 256 ? 2 : 3; }
+// Row-tile kernel shape per head_dim: waves per workgroup and 16-column MFMA
+// n-tiles per wave.  head_dim 256: 8 waves (two per SIMD) of 16 columns, so
+// each wave fits in 256 registers and the SIMD interleaves two waves;
+// head_dim 128: 4 waves of 48 columns.  Both give a workgroup 128 or 192
+// columns sharing one set of K/V tiles.
+constexpr int prefill_waves(int head_dim) { return head_dim >= 256 ? 8 : 4; }
+constexpr int prefill_ntiles(int head_dim) { return head_dim >= 256 ? 1 : 3; }
 
 struct StreamArg {
   int32_t layout;       // 0 paged, 1 slab

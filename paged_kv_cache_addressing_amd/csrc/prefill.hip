@@ -68,7 +68,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int KV, int D>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
+__global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const PrefillArgs A) {
   // A workgroup owns one kv head g, HW = heads_per_wg of its q heads (head
   // group hg) and a tile of rpt rows: its 4*16*NT columns, numbered
   // c = 16*NT*wave + 16*nt + n, are the (row, head) pairs (c / HW, c % HW).
@@ -78,10 +78,12 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   constexpr int KS = D / 32;            // QK k-steps
   constexpr int MD = D / 16;            // O^T m-tiles
   constexpr int NT = prefill_ntiles(D);  // 16-column n-tiles per wave
+  constexpr int NW = prefill_waves(D);   // waves per workgroup
+  constexpr int NTH = 64 * NW;          // threads per workgroup
   constexpr int KF = MT * KS;           // K fragments (1 KiB) per step
   constexpr int VF = MD;                // V fragments per step
-  constexpr int KPW = KF / 4;           // DMA fragments per wave per step
-  constexpr int VPW = VF / 4;
+  constexpr int KPW = KF / NW;          // DMA fragments per wave per step
+  constexpr int VPW = VF / NW;
   constexpr int NSLOT = 3;
   constexpr int KSLOT = KF * 64;        // 16-byte entries per slot
   constexpr int VSLOT = VF * 64;
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   constexpr int KST = KF * 64 / 2;
   constexpr int VST = VF * 64 / 2;
   constexpr int NSTG = 3;
-  constexpr int K8PW = KST / 256;       // fp8 DMAs per wave per step
-  constexpr int V8PW = VST / 256;
+  constexpr int K8PW = KST / NTH;       // fp8 DMAs per wave per step
+  constexpr int V8PW = VST / NTH;
   static_assert(kPage % BK == 0, "a step never straddles two pages");
 
   __shared__ v4u lds[NSLOT * (KSLOT + VSLOT) + (KV ? NSTG * (KST + VST) : 0)];
@@ -225,8 +227,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
   auto zero_tail_bf16 = [&](int v, int sl) {
     v4u* Ls = Vbase + sl * VSLOT;
 #pragma unroll
-    for (int i = 0; i < VSLOT / 256; ++i) {
-      const int q = i * 256 + tid, lp = q & 63;
+    for (int i = 0; i < VSLOT / NTH; ++i) {
+      const int q = i * NTH + tid, lp = q & 63;
       Ls[q] = keep_first_h(Ls[q], n_keys_t - (v * BK + 8 * (lp >> 4)));
     }
   };
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
 #pragma unroll
     for (int i = 0; i < K8PW; ++i) {
       // entry fp*64 + lane: 16 dims (two QK k-steps) of one S^T row
-      const int fp = 4 * i + wave, mt = fp / (KS / 2), kq = fp % (KS / 2);
+      const int fp = NW * i + wave, mt = fp / (KS / 2), kq = fp % (KS / 2);
       const int off = (krow + 4 * mt) * D + 64 * kq + 16 * a;
       __builtin_amdgcn_global_load_lds(base + off, dst + fp * 64, 16, 0, 0);
     }
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       // entry q: 16 keys (half h of the step) of dim 16*md + dl
       // (the offset is named first: a call nested in the builtin's argument
       // list makes the host pass drop the kernel's launch stub)
-      const int q = i * 256 + tid, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
+      const int q = i * NTH + tid, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
       const int off = v_off<D, ESZ>(o + 16 * h, 16 * md + dl);
       __builtin_amdgcn_global_load_lds(T.v + off, dst + (q >> 6) * 64, 16, 0, 0);
     }
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       v4u* Ls = Kbase + slk * KSLOT;
 #pragma unroll
       for (int i = 0; i < K8PW; ++i) {
-        const int fp = 4 * i + wave, mt = fp / (KS / 2), kq = fp % (KS / 2);
+        const int fp = NW * i + wave, mt = fp / (KS / 2), kq = fp % (KS / 2);
         const int f0 = mt * KS + 2 * kq;
         const v4u x = St[fp * 64 + lane];
         Ls[f0 * 64 + lane] = __builtin_bit_cast(v4u, fp8x8_to_bf16(x[0], x[1]));
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
       const bool tail = decltype(may_tail)::value && vv * BK + BK > n_keys_t;
 #pragma unroll
       for (int i = 0; i < V8PW; ++i) {
-        const int q = i * 256 + tid, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
+        const int q = i * NTH + tid, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
         v4u x = St[q];
         if (tail) x = keep_first_b(x, n_keys_t - (vv * BK + 16 * h));
         Ls[md * 64 + 32 * h + dl] = __builtin_bit_cast(v4u, fp8x8_to_bf16(x[0], x[1]));
@@ -596,11 +598,12 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs A) {
 template <int KV, int D>
 static int launch_prefill_t(const PrefillArgs& A, hipStream_t st) {
   dim3 grid((unsigned)(A.total_tiles * A.cache.n_kv_heads * (A.group / A.heads_per_wg)));
-  hipLaunchKernelGGL((prefill_kernel<KV, D>), grid, dim3(256), 0, st, A);
+  hipLaunchKernelGGL((prefill_kernel<KV, D>), grid, dim3(64 * prefill_waves(D)), 0, st, A);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
 int prefill_columns(int head_dim) { return 16 * prefill_ntiles(head_dim); }
+int prefill_wg_columns(int head_dim) { return prefill_waves(head_dim) * prefill_columns(head_dim); }
 
 int launch_prefill(const PrefillArgs& A, int kv_dtype, int head_dim, hipStream_t st) {
   if (kv_dtype == 0 && head_dim == 128) return launch_prefill_t<0, 128>(A, st);
