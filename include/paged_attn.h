@@ -59,6 +59,8 @@ extern "C" {
 #define PA_DEFAULT_SPLIT_KEYS 4096
 /* Most query rows per stream one decode call serves (verify rows). */
 #define PA_DECODE_MAX_ROWS 16
+/* Most rows of a stream that carries an ancestor table (one 32-bit word per row). */
+#define PA_TREE_MAX_ROWS 32
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -114,6 +116,15 @@ typedef struct pa_kv_cache {
  * multiple of 256), same dtype as the cache: K element (g*C + t)*head_dim + d;
  * V element g*C*head_dim + ((t/VB)*head_dim + d)*VB + t%VB (the page layout
  * of V repeated over the slab).
+ *
+ * Ancestor table (tree-shaped speculative verify; TensorFold pull request
+ * #1355, follow-up checks, "Indexing", names a per-row ancestor table beside
+ * the query rows): when tree_mask is set (device, n_rows 32-bit words,
+ * n_rows <= PA_TREE_MAX_ROWS), row i attends every key before first_pos and,
+ * of the rows' own keys, position first_pos + j (j <= i) only when bit j of
+ * word i is set; bits above i are ignored.  The rows' K/V are stored in
+ * topological order (a node after its parent).  Every row must attend at
+ * least one key (set bit i, or have first_pos > 0).  NULL: the causal chain.
  */
 typedef struct pa_stream {
   int32_t layout;          /* pa_layout */
@@ -126,6 +137,7 @@ typedef struct pa_stream {
   void *k_slab;            /* device (slab layout) */
   void *v_slab;            /* device (slab layout) */
   int64_t slab_cap;        /* slab capacity in positions (slab layout) */
+  const uint32_t *tree_mask; /* device ancestor words, or NULL (see above) */
 } pa_stream;
 
 /* Text for a pa_status value (static storage). */

@@ -57,10 +57,10 @@ def _load():
         lib.oracle_gather.argtypes = [P, P, i32, f64, f64, P, i64, i32, i32, i64, P, P]
         lib.oracle_attention.restype = i32
         lib.oracle_attention.argtypes = [P, P, i32, f64, f64, P, i64, i32, i32, i64, P, i32, i64,
-                                         P, i32, f64, P, i32]
+                                         P, P, i32, f64, P, i32]
         lib.oracle_attention_split.restype = i32
         lib.oracle_attention_split.argtypes = [P, P, i32, f64, f64, P, i64, i32, i32, i64, P, i32,
-                                               i64, P, i32, f64, i64, i64, P, P, P, i32]
+                                               i64, P, P, i32, f64, i64, i64, P, P, P, i32]
         lib.oracle_merge.restype = i32
         lib.oracle_merge.argtypes = [P, P, P, i64, i64, i32, P]
         _lib = lib
@@ -134,11 +134,14 @@ def gather(k_src, v_src, dtype, n_kv_heads, head_dim, n_keys, page_table=None, p
 
 def attention(k_src, v_src, dtype, q_bits, first_pos, n_kv_heads, n_keys_stored,
               page_table=None, page_stride=0, rows=None, sm_scale=None, k_scale=1.0,
-              v_scale=1.0, n_threads=0):
+              v_scale=1.0, n_threads=0, tree=None):
     """Float64 attention output ``[n_sel][Hq][D]`` for selected rows of one stream.
 
     q_bits: bf16 bits ``[n_rows][Hq][D]``; row i is at position first_pos + i
     and sees keys 0..first_pos+i.  ``rows`` selects row indices (default all).
+    tree: optional ancestor words (uint32, one per row, at most 32 rows): row
+    i then sees the keys before first_pos and the key first_pos + j (j <= i)
+    only where bit j of its word is set.
     """
     q = _c(q_bits, np.uint16)
     n_rows, hq, d = q.shape
@@ -147,10 +150,12 @@ def attention(k_src, v_src, dtype, q_bits, first_pos, n_kv_heads, n_keys_stored,
         sm_scale = 1.0 / np.sqrt(d)
     out = np.empty((len(sel), hq, d), np.float64)
     pt = _c(page_table, np.int32)
+    tr = _c(tree, np.uint32)
     rc = _load().oracle_attention(_ptr(k_src), _ptr(v_src), dtype, float(k_scale),
                                   float(v_scale), _ptr(pt), int(page_stride), n_kv_heads, d,
-                                  int(n_keys_stored), _ptr(q), hq, int(first_pos), _ptr(sel),
-                                  len(sel), float(sm_scale), _ptr(out), int(n_threads))
+                                  int(n_keys_stored), _ptr(q), hq, int(first_pos), _ptr(tr),
+                                  _ptr(sel), len(sel), float(sm_scale), _ptr(out),
+                                  int(n_threads))
     if rc != 0:
         raise ValueError(f"oracle_attention failed ({rc})")
     return out
@@ -158,7 +163,7 @@ def attention(k_src, v_src, dtype, q_bits, first_pos, n_kv_heads, n_keys_stored,
 
 def attention_split(k_src, v_src, dtype, q_bits, first_pos, n_kv_heads, n_keys_stored,
                     split_keys, n_split, page_table=None, page_stride=0, rows=None,
-                    sm_scale=None, k_scale=1.0, v_scale=1.0, n_threads=0):
+                    sm_scale=None, k_scale=1.0, v_scale=1.0, n_threads=0, tree=None):
     """Split-K form: (m, l, o) per (row, head, split) in float64."""
     q = _c(q_bits, np.uint16)
     n_rows, hq, d = q.shape
@@ -169,10 +174,12 @@ def attention_split(k_src, v_src, dtype, q_bits, first_pos, n_kv_heads, n_keys_s
     l = np.empty_like(m)
     o = np.empty((len(sel), hq, n_split, d), np.float64)
     pt = _c(page_table, np.int32)
+    tr = _c(tree, np.uint32)
     rc = _load().oracle_attention_split(_ptr(k_src), _ptr(v_src), dtype, float(k_scale),
                                         float(v_scale), _ptr(pt), int(page_stride), n_kv_heads,
                                         d, int(n_keys_stored), _ptr(q), hq, int(first_pos),
-                                        _ptr(sel), len(sel), float(sm_scale), int(split_keys),
+                                        _ptr(tr), _ptr(sel), len(sel), float(sm_scale),
+                                        int(split_keys),
                                         int(n_split), _ptr(m), _ptr(l), _ptr(o), int(n_threads))
     if rc != 0:
         raise ValueError(f"oracle_attention_split failed ({rc})")

@@ -9,9 +9,9 @@
  *
  * What it computes, and where the pages define it:
  *   - Each query head reads the key head it belongs to (TensorFold pull
- *     request #1373, "What changes": the tiles "take the key head").  The
- *     grouping itself is not spelled out; the reading used here is
- *     g = floor(h / G), G = n_q_heads / n_kv_heads.
+ *     request #1373, "What changes": each tile reads its query head's key
+ *     head).  The grouping itself is not spelled out; the reading used here
+ *     is g = floor(h / G), G = n_q_heads / n_kv_heads.
  *   - A paged stream's key at position t lives in page PT[t / 256], slot
  *     t mod 256, head-major inside the page: element offset
  *     PT[t/256]*PS + (g*256 + t mod 256)*D + d (pull request #2011, review
@@ -26,6 +26,13 @@
  *     sees keys 0..first_pos+i inclusive (causal rows against the paged
  *     prefix: pull request #1373, prompt rows; keys past the limit land as
  *     zeros: pull request #2011 review).
+ *   - Speculative verify rows may carry a per-row ancestor table (pull
+ *     request #1355, follow-up checks, "Indexing": the partial and merge
+ *     kernels index a row table of ancestors beside the query rows).  The
+ *     pages name the table only; the reading used here is one 32-bit word
+ *     per row (at most 32 rows): keys before the stream's first row stay
+ *     visible, and row i sees key first_pos + j (j <= i) when bit j is set.
+ *     Without the table, rows are the causal chain above.
  *   - Decode is split-K partials plus a merge (issue #1344, "Mechanism":
  *     partial then attn_merge).  oracle_attention_split and oracle_merge give
  *     the split form, in the same float64 arithmetic, for the merge self-check.
@@ -241,6 +248,7 @@ typedef struct {
   int n_kv_heads, n_q_heads, head_dim;
   const uint16_t *q;       /* [rows][Hq][D] bf16 bits */
   int64_t first_pos;
+  const uint32_t *tree;    /* NULL: causal chain; else one ancestor word per row */
   const int32_t *rows;     /* selected row indices */
   int n_sel;
   double sm_scale;
@@ -252,8 +260,22 @@ typedef struct {
   pthread_mutex_t lock;
 } oracle_job;
 
-/* One (row, q head): z_t = sm_scale * <q, k_t> for t <= pos, then either the
- * softmax-weighted sum of v_t, or per split j the triple
+/* Whether row `row` (at position first_pos + row) attends key t.  Causal
+ * rows see every key up to their own position.  With an ancestor table
+ * (tree-shaped speculative verify), the keys before the stream's rows stay
+ * visible and among the rows' own keys first_pos + j (j <= row) only those
+ * whose bit j is set in the row's word are: a draft token attends the
+ * tokens on its path from the root, itself included when bit row is set. */
+static int oracle_visible(const oracle_job *J, int64_t row, int64_t t) {
+  int64_t j;
+  if (t > J->first_pos + row) return 0;
+  if (!J->tree || t < J->first_pos) return 1;
+  j = t - J->first_pos;
+  return (int)((J->tree[row] >> j) & 1u);
+}
+
+/* One (row, q head): z_t = sm_scale * <q, k_t> for the visible keys t, then
+ * either the softmax-weighted sum of v_t, or per split j the triple
  * (m_j = max z, l_j = sum exp(z - m_j), o_j = sum exp(z - m_j) v_t). */
 static void oracle_one(oracle_job *J, int64_t task, double *z, double *qd) {
   int sel = (int)(task / J->n_q_heads);
@@ -279,10 +301,12 @@ static void oracle_one(oracle_job *J, int64_t task, double *z, double *qd) {
     double mx = -INFINITY, den = 0.0;
     double *o = J->out + ((int64_t)sel * J->n_q_heads + h) * D;
     for (int64_t t = 0; t < nvis; ++t)
-      if (z[t] > mx) mx = z[t];
+      if (oracle_visible(J, row, t) && z[t] > mx) mx = z[t];
     for (int d = 0; d < D; ++d) o[d] = 0.0;
     for (int64_t t = 0; t < nvis; ++t) {
-      double e = exp(z[t] - mx);
+      double e;
+      if (!oracle_visible(J, row, t)) continue;
+      e = exp(z[t] - mx);
       den += e;
       for (int d = 0; d < D; ++d) o[d] += e * V[t * D + d];
     }
@@ -299,9 +323,11 @@ static void oracle_one(oracle_job *J, int64_t task, double *z, double *qd) {
     if (hi > nvis) hi = nvis;
     for (int d = 0; d < D; ++d) o[d] = 0.0;
     for (int64_t t = lo; t < hi; ++t)
-      if (z[t] > mx) mx = z[t];
+      if (oracle_visible(J, row, t) && z[t] > mx) mx = z[t];
     for (int64_t t = lo; t < hi; ++t) {
-      double e = exp(z[t] - mx);
+      double e;
+      if (!oracle_visible(J, row, t)) continue;
+      e = exp(z[t] - mx);
       den += e;
       for (int d = 0; d < D; ++d) o[d] += e * V[t * D + d];
     }
@@ -360,7 +386,8 @@ static int oracle_prepare(oracle_job *J, const void *k_src, const void *v_src, i
                           double k_scale, double v_scale, const int32_t *page_table,
                           int64_t page_stride, int n_kv_heads, int head_dim,
                           int64_t n_keys_stored, const uint16_t *q, int n_q_heads,
-                          int64_t first_pos, const int32_t *rows, int n_sel, double sm_scale,
+                          int64_t first_pos, const uint32_t *tree, const int32_t *rows,
+                          int n_sel, double sm_scale,
                           double **kbuf, double **vbuf) {
   int64_t max_row = -1, need;
   int i;
@@ -370,6 +397,7 @@ static int oracle_prepare(oracle_job *J, const void *k_src, const void *v_src, i
     if (rows[i] < 0) return -1;
     if (rows[i] > max_row) max_row = rows[i];
   }
+  if (tree && max_row >= 32) return -1; /* one 32-bit ancestor word per row */
   need = first_pos + max_row + 1;
   if (n_sel > 0 && need > n_keys_stored) return -2;
   if (need < 1) need = 1;
@@ -388,6 +416,7 @@ static int oracle_prepare(oracle_job *J, const void *k_src, const void *v_src, i
   J->head_dim = head_dim;
   J->q = q;
   J->first_pos = first_pos;
+  J->tree = tree;
   J->rows = rows;
   J->n_sel = n_sel;
   J->sm_scale = sm_scale;
@@ -400,13 +429,14 @@ static int oracle_prepare(oracle_job *J, const void *k_src, const void *v_src, i
 int oracle_attention(const void *k_src, const void *v_src, int dtype, double k_scale,
                      double v_scale, const int32_t *page_table, int64_t page_stride,
                      int n_kv_heads, int head_dim, int64_t n_keys_stored, const uint16_t *q,
-                     int n_q_heads, int64_t first_pos, const int32_t *rows, int n_sel,
-                     double sm_scale, double *out, int n_threads) {
+                     int n_q_heads, int64_t first_pos, const uint32_t *tree,
+                     const int32_t *rows, int n_sel, double sm_scale, double *out,
+                     int n_threads) {
   oracle_job J;
   double *kb = NULL, *vb = NULL;
   int rc = oracle_prepare(&J, k_src, v_src, dtype, k_scale, v_scale, page_table, page_stride,
-                          n_kv_heads, head_dim, n_keys_stored, q, n_q_heads, first_pos, rows,
-                          n_sel, sm_scale, &kb, &vb);
+                          n_kv_heads, head_dim, n_keys_stored, q, n_q_heads, first_pos, tree,
+                          rows, n_sel, sm_scale, &kb, &vb);
   if (rc == 0) {
     J.out = out;
     rc = oracle_run(&J, n_threads);
@@ -422,16 +452,16 @@ int oracle_attention_split(const void *k_src, const void *v_src, int dtype, doub
                            double v_scale, const int32_t *page_table, int64_t page_stride,
                            int n_kv_heads, int head_dim, int64_t n_keys_stored,
                            const uint16_t *q, int n_q_heads, int64_t first_pos,
-                           const int32_t *rows, int n_sel, double sm_scale, int64_t split_keys,
-                           int64_t n_split, double *m_out, double *l_out, double *o_out,
-                           int n_threads) {
+                           const uint32_t *tree, const int32_t *rows, int n_sel,
+                           double sm_scale, int64_t split_keys, int64_t n_split, double *m_out,
+                           double *l_out, double *o_out, int n_threads) {
   oracle_job J;
   double *kb = NULL, *vb = NULL;
   int rc;
   if (split_keys <= 0 || n_split <= 0) return -1;
   rc = oracle_prepare(&J, k_src, v_src, dtype, k_scale, v_scale, page_table, page_stride,
-                      n_kv_heads, head_dim, n_keys_stored, q, n_q_heads, first_pos, rows, n_sel,
-                      sm_scale, &kb, &vb);
+                      n_kv_heads, head_dim, n_keys_stored, q, n_q_heads, first_pos, tree, rows,
+                      n_sel, sm_scale, &kb, &vb);
   if (rc == 0) {
     int i;
     for (i = 0; i < n_sel; ++i)

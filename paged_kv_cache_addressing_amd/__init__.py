@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
 PAGE_POSITIONS = 256
 DEFAULT_SPLIT_KEYS = 4096
 DECODE_MAX_ROWS = 16
+TREE_MAX_ROWS = 32  # rows of a stream that carries an ancestor table
 
 PA_OK, PA_EINVAL, PA_ERANGE, PA_ENOSPC, PA_ETOOBIG, PA_EWORKSPACE, PA_EDEVICE, PA_EUNSUPPORTED = (
     0, -1, -2, -3, -4, -5, -6, -7)
@@ -52,7 +53,7 @@ class pa_stream(C.Structure):
     _fields_ = [("layout", C.c_int32), ("ctx_len", C.c_int32), ("n_rows", C.c_int32),
                 ("row_offset", C.c_int32), ("first_pos", C.c_int32), ("reserved", C.c_int32),
                 ("page_table", C.c_void_p), ("k_slab", C.c_void_p), ("v_slab", C.c_void_p),
-                ("slab_cap", C.c_int64)]
+                ("slab_cap", C.c_int64), ("tree_mask", C.c_void_p)]
 
 
 class pa_decode_plan(C.Structure):
@@ -173,11 +174,13 @@ class Stream:
     v_slab: object = None         # device tensor [Hkv][cap/VB][D][VB]
     slab_cap: int = 0
     layout: int = PA_LAYOUT_PAGED
+    tree_mask: object = None      # int32 device tensor, one ancestor word per row
 
     def c(self) -> pa_stream:
         return pa_stream(int(self.layout), int(self.ctx_len), int(self.n_rows),
                          int(self.row_offset), int(self.first_pos), 0, _ptr(self.page_table),
-                         _ptr(self.k_slab), _ptr(self.v_slab), int(self.slab_cap))
+                         _ptr(self.k_slab), _ptr(self.v_slab), int(self.slab_cap),
+                         _ptr(self.tree_mask))
 
 
 def _streams(streams):

@@ -44,6 +44,7 @@ int check_streams_shape(const pa_stream* s, int32_t n, int32_t n_q_heads, int32_
     if (t.ctx_len < 1 || t.n_rows < 0 || t.first_pos < 0 || t.row_offset < 0) return PA_EINVAL;
     if ((int64_t)t.first_pos + t.n_rows > t.ctx_len) return PA_ERANGE;
     if (max_rows > 0 && t.n_rows > max_rows) return PA_EINVAL;
+    if (t.tree_mask && t.n_rows > PA_TREE_MAX_ROWS) return PA_EINVAL;
     if (t.n_rows > 0) spans.emplace_back(t.row_offset, (int64_t)t.row_offset + t.n_rows);
   }
   std::sort(spans.begin(), spans.end());
@@ -88,6 +89,7 @@ pa::StreamArg stream_arg(const pa_kv_cache* c, const pa_stream& t) {
   a.first_pos = t.first_pos;
   a.n_keys = t.first_pos + t.n_rows;
   a.page_table = t.page_table;
+  a.tree_mask = t.tree_mask;
   if (t.layout == PA_LAYOUT_PAGED) {
     a.k_base = static_cast<uint8_t*>(c ? c->k_pages : nullptr);
     a.v_base = static_cast<uint8_t*>(c ? c->v_pages : nullptr);
@@ -221,7 +223,7 @@ const char* pa_status_string(int status) {
   }
 }
 
-int pa_version(void) { return (1 << 16) | 0; }
+int pa_version(void) { return (1 << 16) | 1; }
 
 int page_pool_create(int32_t n_pages, pa_page_pool** out) {
   if (!out || n_pages < 1) return PA_EINVAL;

@@ -67,6 +67,10 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(const DecodeArgs
   const bool col_ok = r < S.n_rows;
   const int pos = col_ok ? S.first_pos + r : S.n_keys - 1;
   const int h = g * G + hl;
+  // Visible keys of the column's row: all up to pos; with an ancestor table,
+  // of the rows' own keys first_pos + j only those whose bit j is set.
+  const uint32_t anc = (S.tree_mask && col_ok) ? S.tree_mask[r] : 0xFFFFFFFFu;
+  const int mask_from = S.tree_mask ? S.first_pos : S.first_pos + 1;  // first maskable key
 
   v8bf qb[KS];
   {
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(const DecodeArgs
 
       // Online softmax for this lane's column over its 4*MT keys.
       const int kabs0 = p * kPage + c0 + 8 * KK * a;
-      const bool need_mask = p * kPage + c0 + CK - 1 > S.first_pos;
+      const bool need_mask = p * kPage + c0 + CK - 1 >= mask_from;
       float sv[MT][4];
       float mx = -INFINITY;
 #pragma unroll
@@ -143,7 +147,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(const DecodeArgs
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = sacc[mt][i] * A.scale_log2;
-          if (need_mask && kabs0 + 4 * mt + i > pos) v = -INFINITY;
+          const int kabs = kabs0 + 4 * mt + i, rel = kabs - S.first_pos;
+          const bool vis = (kabs <= pos) & ((rel < 0) | (((anc >> (rel & 31)) & 1u) != 0u));
+          if (need_mask && !vis) v = -INFINITY;
           sv[mt][i] = v;
           mx = fmaxf(mx, v);
         }

@@ -32,6 +32,7 @@ struct StreamArg {
   uint8_t* k_base;      // paged: pool K base; slab: slab K base
   uint8_t* v_base;      // paged: pool V base; slab: slab V base
   int64_t slab_cap;     // slab: capacity in positions (multiple of 256)
+  const uint32_t* tree_mask;  // ancestor words per row, or null (causal chain)
 };
 
 struct CacheArg {

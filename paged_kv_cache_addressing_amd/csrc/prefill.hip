@@ -135,9 +135,13 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   const int v_lo = k_lo / BK;
   const int v_hi = k_end > k_lo ? (k_end + BK - 1) / BK : v_lo;
   const bool wave_active = wave * 16 * NT < rows_here * HW;
+  // first key some row of the tile may not see: past the first row's own
+  // position, or (ancestor table) the stream's first row key
+  const int mask_from = S.tree_mask ? S.first_pos : pos_first + 1;
 
   // Columns of this wave.
   int crow[NT], chead[NT], cpos[NT];
+  uint32_t canc[NT];  // ancestor word of the column's row (all ones: causal chain)
   bool cok[NT];
   v8bf qb[NT][KS];
 #pragma unroll
@@ -148,6 +152,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
     crow[nt] = row0 + rl;
     cok[nt] = rl < rows_here;
     cpos[nt] = cok[nt] ? S.first_pos + crow[nt] : pos_last;
+    canc[nt] = (S.tree_mask && cok[nt]) ? S.tree_mask[crow[nt]] : 0xFFFFFFFFu;
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(A.q) +
                         ((int64_t)(S.row_offset + (cok[nt] ? crow[nt] : row0)) * A.n_q_heads +
                          (cok[nt] ? chead[nt] : h0)) * D * 2;
@@ -314,8 +319,14 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (kabs0 + 4 * mt + i > cpos[nt]) Sx[mt][nt][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          // branch-free: a select per logit (nested conditions here were
+          // compiled into control flow that dropped the ancestor test)
+          const int kabs = kabs0 + 4 * mt + i, rel = kabs - S.first_pos;
+          const bool anc_ok = (rel < 0) | (((canc[nt] >> (rel & 31)) & 1u) != 0u);
+          const bool vis = (kabs <= cpos[nt]) & anc_ok;
+          Sx[mt][nt][i] = vis ? Sx[mt][nt][i] : -INFINITY;
+        }
   };
 
   // S(v+1) = K(v+1) Q^T on the matrix cores with the softmax of S(v) on the
@@ -450,7 +461,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       if (FAST || v + 3 < v_hi) dma8_v(v + 3, r0);
     }
     if (wave_active) {
-      if (!FAST && v * BK + BK - 1 > pos_first) mask(v, Sc);
+      if (!FAST && v * BK + BK - 1 >= mask_from) mask(v, Sc);
       v8bf P[NT];
       float alpha[NT];
       // K(v+1), or stale data past the end (unused)
@@ -528,9 +539,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
     __syncthreads();
 
     // Steps [v_lo, v_fast) are steady state: v+3 (bf16) or v+4 (fp8) is
-    // still in range, no key of the step is past the first row's position,
+    // still in range, no key of the step is maskable (before mask_from),
     // and the next V step holds no key at or past n_keys_t.
-    const int v_fast = max(v_lo, min(min(v_hi - (KV ? 4 : 3), (pos_first + 1) / BK),
+    const int v_fast = max(v_lo, min(min(v_hi - (KV ? 4 : 3), mask_from / BK),
                                      n_keys_t / BK - 1));
     // The steady state runs three steps per iteration, one per ring
     // position, so every slot address is a constant; S(v+1) alternates

@@ -8,6 +8,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 from . import (PA_LAYOUT_PAGED, PA_LAYOUT_SLAB, PAGE_POSITIONS, KVCache, Stream, alloc_pool,
@@ -34,6 +35,13 @@ def _store(cache, descs, rows_k, rows_v, device):
     v = torch.cat(rows_v).to(device)
     write_kv(cache, descs, k, v)
     del k, v
+
+
+def _tree(st, device):
+    """The stream's ancestor words as a device int32 tensor, or None."""
+    if getattr(st, "tree", None) is None:
+        return None
+    return torch.from_numpy(st.tree.view(np.int32).copy()).to(device)
 
 
 def upload(wl, device: str = "cuda", poison_tail: bool = False,
@@ -71,7 +79,7 @@ def upload(wl, device: str = "cuda", poison_tail: bool = False,
                         cache.v_pages[last, :, b, :, start:] = nan
             desc = Stream(st.ctx_len, st.ctx_len, at, 0, page_table=pt, layout=PA_LAYOUT_PAGED)
             att = Stream(st.ctx_len, st.n_rows, st.row_offset, st.first_pos, page_table=pt,
-                         layout=PA_LAYOUT_PAGED)
+                         layout=PA_LAYOUT_PAGED, tree_mask=_tree(st, device))
         else:
             ks, vs = alloc_slab(st.slab_cap, hkv, d, wl.kv_dtype, device, zero=True)
             tables.append(None)
@@ -79,7 +87,8 @@ def upload(wl, device: str = "cuda", poison_tail: bool = False,
             desc = Stream(st.ctx_len, st.ctx_len, at, 0, k_slab=ks, v_slab=vs,
                           slab_cap=st.slab_cap, layout=PA_LAYOUT_SLAB)
             att = Stream(st.ctx_len, st.n_rows, st.row_offset, st.first_pos, k_slab=ks, v_slab=vs,
-                         slab_cap=st.slab_cap, layout=PA_LAYOUT_SLAB)
+                         slab_cap=st.slab_cap, layout=PA_LAYOUT_SLAB,
+                         tree_mask=_tree(st, device))
         store_descs.append(desc)
         rk.append(wl.k_rows[s])
         rv.append(wl.v_rows[s])

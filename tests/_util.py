@@ -63,11 +63,11 @@ def oracle_reference(wl, s, rows=None, pool=None, n_threads=0):
         return oracle.attention(kp, vp, dt, q, st.first_pos, wl.n_kv_heads, st.ctx_len,
                                 page_table=st.pages, page_stride=ps, rows=rows,
                                 sm_scale=wl.sm_scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
-                                n_threads=n_threads)
+                                n_threads=n_threads, tree=st.tree)
     k, v = oracle_logical(wl, s)
     return oracle.attention(k, v, dt, q, st.first_pos, wl.n_kv_heads, st.ctx_len, rows=rows,
                             sm_scale=wl.sm_scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
-                            n_threads=n_threads)
+                            n_threads=n_threads, tree=st.tree)
 
 
 def gpu_v_layout(v_rows: np.ndarray, vb: int) -> np.ndarray:

@@ -367,3 +367,65 @@ def test_decode_partials_match_oracle_split_form(dtype):
         np.testing.assert_allclose(go[vis] / gl[vis][..., None] * vs, o[vis] / l[vis][..., None],
                                    rtol=0, atol=(2e-2 if dtype == "bf16" else 6e-2))
         base += n
+
+
+# ----------------------------------------------------------------------------- draft-tree rows
+
+TREE_DECODE_CASES = [
+    # name, Hq, Hkv, D, dtype, ctx_lens, rows, layouts, split
+    ("tree-wide-bf16-mixed", 24, 4, 256, "bf16", [4100, 9000, 700], [16, 16, 7],
+     ["paged", "slab", "paged"], 4096),
+    ("tree-wide-fp8", 24, 4, 256, "fp8", [6000, 4096 + 10], [16, 12], None, 4096),
+    ("tree-narrow-d128", 12, 2, 128, "bf16", [2000, 1030], [3, 5], None, 1024),
+    ("tree-wide-d128-fp8", 12, 2, 128, "fp8", [3000], [16], None, 1024),
+]
+
+
+@pytest.mark.parametrize("case", TREE_DECODE_CASES, ids=[c[0] for c in TREE_DECODE_CASES])
+def test_tree_decode_matches_oracle(case):
+    name, hq, hkv, d, dtype, lens, rows, layouts, split = case
+    wl = workloads.build(name, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, kv_dtype=dtype,
+                         ctx_lens=lens, n_rows=rows, layouts=layouts, seed=81,
+                         split_keys=split, trees=["random"] * len(lens))
+    say(f"tree decode {name}")
+    res = upload(wl, poison_tail=True)
+    out = decode(res)
+    refs, sels = references(wl)
+    err = launch_error(wl, out, refs, sels)
+    say(f"tree decode {name}: normalised error {err:.3e}")
+    assert err <= tol(wl)
+    # the tree changes the result (the control: the causal rows differ)
+    causal = decode(upload(workloads.build(name, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                                           kv_dtype=dtype, ctx_lens=lens, n_rows=rows,
+                                           layouts=layouts, seed=81, split_keys=split)))
+    assert not same_bytes(causal, out)
+
+
+@pytest.mark.parametrize("dtype,d,rows", [("bf16", 256, 32), ("fp8", 256, 20), ("bf16", 128, 29)])
+def test_tree_prefill_matches_oracle(dtype, d, rows):
+    wl = workloads.build("tree-prefill", n_q_heads=8 if d == 128 else 6, n_kv_heads=2,
+                         head_dim=d, kv_dtype=dtype, ctx_lens=[900, 333], n_rows=[rows, 7],
+                         layouts=["paged", "slab"], seed=82, trees=["random", "random"])
+    res = upload(wl, poison_tail=True)
+    out = prefill(res)
+    refs, sels = references(wl)
+    err = launch_error(wl, out, refs, sels)
+    say(f"tree prefill {dtype} d{d}: normalised error {err:.3e}")
+    assert err <= tol(wl)
+
+
+def test_chain_tree_gives_the_causal_bytes_and_trees_are_batch_invariant():
+    kw = dict(n_q_heads=24, n_kv_heads=4, head_dim=256, kv_dtype="bf16",
+              ctx_lens=[5000, 4097, 800], n_rows=[16, 3, 16], seed=83)
+    plain = upload(workloads.build("chain", **kw))
+    chain = upload(workloads.build("chain", trees=["chain"] * 3, **kw))
+    assert same_bytes(decode(chain), decode(plain))
+    assert same_bytes(prefill(chain), prefill(plain))
+    tree = upload(workloads.build("tree", trees=["random", None, "random"], **kw))
+    both = decode(tree)
+    for st in tree.streams:
+        alone = torch.zeros_like(tree.q)
+        pa.paged_attn_decode(tree.cache, [st], tree.q, out=alone, sm_scale=tree.sm_scale)
+        torch.cuda.synchronize()
+        r0, r1 = st.row_offset, st.row_offset + st.n_rows
+        assert same_bytes(alone[r0:r1], both[r0:r1])

@@ -147,6 +147,8 @@ def test_validation_common(fn):
                                slab_cap=1024)]) == pa.PA_EINVAL
     two = [stream(n_rows=2, first_pos=998), stream(row_offset=1)]  # rows 0-1 and 1 overlap
     assert fn(cache(), two) == pa.PA_ERANGE
+    # an ancestor table covers at most 32 rows (one 32-bit word each)
+    assert fn(cache(), [stream(n_rows=33, first_pos=967, tree_mask=FAKE)]) == pa.PA_EINVAL
     assert fn(cache(), []) == pa.PA_OK  # nothing to do, nothing launched
     assert fn(cache(), [stream(n_rows=0)]) == pa.PA_OK
 

@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import json
 import math
+import random
 import os
 
 import numpy as np
@@ -14,6 +15,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
+import workloads
 from tests._util import bits16
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -283,3 +285,104 @@ def test_row_past_stored_keys_is_refused():
     q, k, v = _rand_case(rng, 4, 2, 16, 10, 2)
     with pytest.raises(ValueError):
         oracle.attention(bits16(k), bits16(v), oracle.DTYPE_BF16, bits16(q), 9, 2, 10)
+
+
+# ----------------------------------------------------------------------------- draft-tree rows
+
+def _tree_mask(parents, first, ctx):
+    """Visibility from the parent list itself (walking up to the prefix):
+    row i sees every key before `first` and the keys of itself and its
+    ancestors -- an independent statement of the ancestor-table rule."""
+    n = len(parents)
+    mask = np.zeros((n, ctx), bool)
+    mask[:, :first] = True
+    for i in range(n):
+        j = i
+        while j >= 0:
+            mask[i, first + j] = True
+            j = parents[j]
+    return torch.from_numpy(mask)
+
+
+def _sdpa_mask(q64, k64, v64, mask, scale):
+    out = F.scaled_dot_product_attention(q64.transpose(0, 1), k64.transpose(0, 1),
+                                         v64.transpose(0, 1), attn_mask=mask, scale=scale,
+                                         enable_gqa=True)
+    return out.transpose(0, 1).numpy()
+
+
+@pytest.mark.parametrize("seed,n_rows,ctx", [(1, 1, 40), (2, 5, 300), (3, 16, 700), (4, 32, 1000)])
+@pytest.mark.parametrize("paged", [False, True])
+def test_tree_rows_match_sdpa_with_ancestor_mask(seed, n_rows, ctx, paged):
+    rng = np.random.default_rng(100 + seed)
+    hq, hkv, d = 6, 2, 32
+    q, k, v = _rand_case(rng, hq, hkv, d, ctx, n_rows)
+    first = ctx - n_rows
+    parents = workloads.random_parents(n_rows, random.Random(seed))
+    words = workloads.tree_words(parents)
+    if paged:
+        n_pages = math.ceil(ctx / PAGE) + 1
+        pt = rng.permutation(n_pages).astype(np.int32)[:math.ceil(ctx / PAGE)]
+        ps = hkv * PAGE * d
+        kp = np.zeros(n_pages * ps, np.uint16)
+        vp = np.zeros(n_pages * ps, np.uint16)
+        oracle.store(kp, vp, oracle.DTYPE_BF16, bits16(k), bits16(v), 0, page_table=pt,
+                     page_stride=ps)
+        got = oracle.attention(kp, vp, oracle.DTYPE_BF16, bits16(q), first, hkv, ctx,
+                               page_table=pt, page_stride=ps, tree=words)
+    else:
+        got = oracle.attention(bits16(k), bits16(v), oracle.DTYPE_BF16, bits16(q), first, hkv,
+                               ctx, tree=words)
+    ref = _sdpa_mask(q.double(), k.double(), v.double(), _tree_mask(parents, first, ctx),
+                     1.0 / math.sqrt(d))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_tree_fp8_rows_match_sdpa_with_ancestor_mask():
+    rng = np.random.default_rng(120)
+    hq, hkv, d, ctx, n = 4, 1, 32, 500, 9
+    q, k, v = _rand_case(rng, hq, hkv, d, ctx, n)
+    ks = float(k.float().abs().max()) / 448
+    vs = float(v.float().abs().max()) / 448
+    kc = np.zeros((ctx, hkv, d), np.uint8)
+    vc = np.zeros_like(kc)
+    oracle.store(kc, vc, oracle.DTYPE_E4M3, bits16(k), bits16(v), 0, k_scale=ks, v_scale=vs)
+    parents = [-1, 0, 0, 1, 1, 2, -1, 6, 3]  # two roots on the prefix
+    got = oracle.attention(kc, vc, oracle.DTYPE_E4M3, bits16(q), ctx - n, hkv, ctx, k_scale=ks,
+                           v_scale=vs, tree=workloads.tree_words(parents))
+    k64 = torch.from_numpy(kc).view(torch.float8_e4m3fn).double() * ks
+    v64 = torch.from_numpy(vc).view(torch.float8_e4m3fn).double() * vs
+    ref = _sdpa_mask(q.double(), k64, v64, _tree_mask(parents, ctx - n, ctx), 1.0 / math.sqrt(d))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_chain_tree_is_exactly_the_causal_rows_and_high_bits_are_ignored():
+    rng = np.random.default_rng(121)
+    q, k, v = _rand_case(rng, 6, 2, 32, 600, 16)
+    causal = oracle.attention(bits16(k), bits16(v), oracle.DTYPE_BF16, bits16(q), 584, 2, 600)
+    chain = workloads.tree_words(list(range(-1, 15)))
+    assert np.array_equal(chain, (1 << np.arange(1, 17, dtype=np.uint64)) - 1)
+    got = oracle.attention(bits16(k), bits16(v), oracle.DTYPE_BF16, bits16(q), 584, 2, 600,
+                           tree=chain)
+    assert np.array_equal(got, causal)
+    # bits above a row's own index name later rows: they are ignored
+    noisy = chain | np.uint32(0xFFFF0000)
+    got2 = oracle.attention(bits16(k), bits16(v), oracle.DTYPE_BF16, bits16(q), 584, 2, 600,
+                            tree=noisy)
+    assert np.array_equal(got2, causal)
+
+
+def test_tree_split_then_merge_equals_direct_and_rows_over_32_are_refused():
+    rng = np.random.default_rng(122)
+    hq, hkv, d, ctx, n = 6, 2, 32, 4100, 16
+    q, k, v = _rand_case(rng, hq, hkv, d, ctx, n)
+    words = workloads.tree_words(workloads.random_parents(n, random.Random(5)))
+    m, l, o = oracle.attention_split(bits16(k), bits16(v), oracle.DTYPE_BF16, bits16(q), ctx - n,
+                                     hkv, ctx, 1024, 5, tree=words)
+    direct = oracle.attention(bits16(k), bits16(v), oracle.DTYPE_BF16, bits16(q), ctx - n, hkv,
+                              ctx, tree=words)
+    np.testing.assert_allclose(oracle.merge(m, l, o), direct, rtol=1e-13, atol=1e-14)
+    q33, k33, v33 = _rand_case(rng, 2, 1, 16, 100, 33)
+    with pytest.raises(ValueError):
+        oracle.attention(bits16(k33), bits16(v33), oracle.DTYPE_BF16, bits16(q33), 67, 1, 100,
+                         tree=np.ones(33, np.uint32))

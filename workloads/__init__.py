@@ -39,6 +39,7 @@ class StreamSpec:
     row_offset: int        # index of the stream's first row in Q / out
     pages: np.ndarray | None = None   # int32 page ids, ceil(ctx_len / 256) of them
     slab_cap: int = 0      # slab capacity in positions (slab layout)
+    tree: np.ndarray | None = None    # uint32 ancestor word per row, or None (causal)
 
 
 @dataclass
@@ -80,12 +81,35 @@ def _scales(ws: list, kind: str) -> float:
     return m / E4M3_MAX if m > 0 else 1.0
 
 
+def tree_words(parents) -> np.ndarray:
+    """Ancestor words of a draft tree given in topological order: parents[i]
+    is the row of node i's parent (< i), or -1 for a node whose parent is the
+    committed prefix.  Bit j of word i is set when row j is node i or one of
+    its ancestors."""
+    words = []
+    for i, p in enumerate(parents):
+        if not (-1 <= p < i):
+            raise ValueError("parents must precede their children")
+        words.append((words[p] if p >= 0 else 0) | (1 << i))
+    return np.asarray(words, dtype=np.uint32)
+
+
+def random_parents(n: int, rng: random.Random) -> list:
+    """A random draft tree over n rows: node 0 hangs off the prefix, every
+    later node off a uniformly drawn earlier node."""
+    return [-1] + [rng.randrange(i) for i in range(1, n)]
+
+
 def build(name: str, *, n_q_heads: int, n_kv_heads: int, head_dim: int, kv_dtype: str,
           ctx_lens: list, n_rows: list, layouts: list | None = None, n_pages: int | None = None,
           seed: int = 0, split_keys: int = 4096, fill_unused: bool = True,
-          sm_scale: float | None = None, slab_cap: int | None = None) -> Workload:
+          sm_scale: float | None = None, slab_cap: int | None = None,
+          trees: list | None = None) -> Workload:
     """Generic generator: one stream per entry of ``ctx_lens``; stream s has
-    ``n_rows[s]`` query rows at its last positions ``ctx-n..ctx-1``."""
+    ``n_rows[s]`` query rows at its last positions ``ctx-n..ctx-1``.
+    ``trees[s]`` (optional): None (causal rows), "chain" (the causal chain as
+    an explicit ancestor table), "random" (a random draft tree drawn from
+    ``random.Random(seed + 7)``, after every torch draw) or a parents list."""
     n_streams = len(ctx_lens)
     layouts = layouts or ["paged"] * n_streams
     g = torch.Generator("cpu").manual_seed(seed)
@@ -118,6 +142,17 @@ def build(name: str, *, n_q_heads: int, n_kv_heads: int, head_dim: int, kv_dtype
     if fill_unused and len(unused):
         fk = _bf16((len(unused) * PAGE, n_kv_heads, head_dim), g)
         fv = _bf16((len(unused) * PAGE, n_kv_heads, head_dim), g)
+    if trees is not None:
+        trng = random.Random(seed + 7)
+        for st, t in zip(streams, trees):
+            if t is None:
+                continue
+            if isinstance(t, str):
+                parents = (list(range(-1, st.n_rows - 1)) if t == "chain"
+                           else random_parents(st.n_rows, trng))
+            else:
+                parents = list(t)
+            st.tree = tree_words(parents)
     ks = vs = 1.0
     if kv_dtype == "fp8":
         ks = _scales(k_rows, "k")
