@@ -165,12 +165,54 @@ PA_API void page_pool_destroy(pa_page_pool *pool);
  * (nothing is claimed), PA_EINVAL for n < 0 or null pointers. */
 PA_API int page_pool_alloc(pa_page_pool *pool, int32_t n, int32_t *ids_out);
 
-/* Return n pages.  PA_ERANGE if an id is out of range or not currently
- * claimed (nothing is freed in that case). */
+/* Shared prefix pages (TensorFold pull request #2011 and the review of #1355
+ * name prefix sharing and a prompt cache that keeps KV pages on the device):
+ * every claimed page carries a reference count, 1 after page_pool_alloc.
+ * page_pool_share adds one reference per occurrence of an id (a second
+ * stream's page table now names the page); page_pool_free drops one per
+ * occurrence, and a page returns to the free set when its count reaches 0.
+ * A stream that must write into a shared partial last page copies it first
+ * (page_copy) into a page of its own: copy on write. */
+
+/* Drop one reference per occurrence of each id.  PA_ERANGE if an id is out
+ * of range or would drop below zero references (nothing changes then). */
 PA_API int page_pool_free(pa_page_pool *pool, const int32_t *ids, int32_t n);
+
+/* Add one reference per occurrence of each id.  PA_ERANGE if an id is out of
+ * range or not claimed (nothing changes then). */
+PA_API int page_pool_share(pa_page_pool *pool, const int32_t *ids, int32_t n);
+
+/* References held on page id (0: free), or a negative status. */
+PA_API int32_t page_pool_refcount(const pa_page_pool *pool, int32_t id);
 
 /* Number of free pages, or a negative status for a NULL pool. */
 PA_API int32_t page_pool_free_count(const pa_page_pool *pool);
+
+/* ----------------------------------------------------------- whole pages
+ * A page is page_stride contiguous elements of K (and of V) starting at
+ * element page*page_stride: every kv head of it, and, when the pool holds
+ * several layers per page (a layer's view is k_pages/v_pages advanced by
+ * its block and the same page_stride, TensorFold pull request #2011,
+ * "Checklist": the layer block lblk inside a page), every layer.
+ * page_stride * element size must be a multiple of 16 bytes.  Page ids are
+ * host arrays of n entries, each in [0, n_pages).
+ *
+ * page_copy: device copy of page src_ids[i] onto dst_ids[i] (K and V) for
+ * every i, enqueued on hip_stream.  Destinations must be distinct and no
+ * destination may be a source of the same call (PA_ERANGE otherwise).
+ *
+ * page_save / page_restore: copies between pages and host memory (pull
+ * request #2011 review: save and restore make one 2D copy per page).  Page
+ * ids[i] occupies bytes [i*P, (i+1)*P) of host_k and of host_v, P =
+ * page_stride * element size; host memory should be pinned for the copies to
+ * run asynchronously on hip_stream.  The caller synchronises before reading
+ * saved pages or reusing restored ones. */
+PA_API int page_copy(const pa_kv_cache *cache, const int32_t *src_ids, const int32_t *dst_ids,
+                     int32_t n, void *hip_stream);
+PA_API int page_save(const pa_kv_cache *cache, const int32_t *ids, int32_t n, void *host_k,
+                     void *host_v, void *hip_stream);
+PA_API int page_restore(const pa_kv_cache *cache, const int32_t *ids, int32_t n,
+                        const void *host_k, const void *host_v, void *hip_stream);
 
 /* ----------------------------------------------------------------- write_kv
  * Store new key/value rows (the step the pages call the rope stores, with

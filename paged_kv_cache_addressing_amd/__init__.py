@@ -32,7 +32,8 @@ PA_KV_BF16, PA_KV_FP8_E4M3 = 0, 1
 PA_LAYOUT_PAGED, PA_LAYOUT_SLAB = 0, 1
 
 EXPORTS = ["pa_status_string", "pa_version", "page_pool_create", "page_pool_destroy",
-           "page_pool_alloc", "page_pool_free", "page_pool_free_count", "write_kv",
+           "page_pool_alloc", "page_pool_free", "page_pool_free_count", "page_pool_share",
+           "page_pool_refcount", "page_copy", "page_save", "page_restore", "write_kv",
            "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_partials",
            "paged_attn_decode_merge", "paged_attn_decode_plan", "paged_attn_prefill"]
 
@@ -89,6 +90,16 @@ def lib():
         L.page_pool_free.argtypes = [P, P, i32]
         L.page_pool_free_count.restype = i32
         L.page_pool_free_count.argtypes = [P]
+        L.page_pool_share.restype = C.c_int
+        L.page_pool_share.argtypes = [P, P, i32]
+        L.page_pool_refcount.restype = i32
+        L.page_pool_refcount.argtypes = [P, i32]
+        L.page_copy.restype = C.c_int
+        L.page_copy.argtypes = [C.POINTER(pa_kv_cache), P, P, i32, P]
+        L.page_save.restype = C.c_int
+        L.page_save.argtypes = [C.POINTER(pa_kv_cache), P, i32, P, P, P]
+        L.page_restore.restype = C.c_int
+        L.page_restore.argtypes = [C.POINTER(pa_kv_cache), P, i32, P, P, P]
         L.write_kv.restype = C.c_int
         L.write_kv.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream), i32, P, P, P]
         L.paged_attn_decode_workspace_size.restype = sz
@@ -246,6 +257,18 @@ class PagePool:
     def free_count(self) -> int:
         return int(lib().page_pool_free_count(self._h))
 
+    def share(self, ids) -> None:
+        """One more reference per occurrence of each id (a shared prefix page)."""
+        a = np.ascontiguousarray(ids, np.int32)
+        _check(lib().page_pool_share(self._h, a.ctypes.data_as(C.c_void_p), len(a)),
+               "page_pool_share")
+
+    def refcount(self, page: int) -> int:
+        r = int(lib().page_pool_refcount(self._h, int(page)))
+        if r < 0:
+            raise PagedAttnError(r, "page_pool_refcount")
+        return r
+
     def close(self):
         if self._h:
             lib().page_pool_destroy(self._h)
@@ -256,6 +279,36 @@ class PagePool:
             self.close()
         except Exception:
             pass
+
+
+def _ids(ids):
+    return np.ascontiguousarray(ids, np.int32)
+
+
+def page_copy(cache: KVCache, src_ids, dst_ids, stream=None) -> None:
+    """Device copy of whole pages src_ids[i] -> dst_ids[i] (K and V)."""
+    s, d = _ids(src_ids), _ids(dst_ids)
+    if len(s) != len(d):
+        raise ValueError("src_ids and dst_ids differ in length")
+    cc = cache.c()
+    _check(lib().page_copy(C.byref(cc), s.ctypes.data_as(C.c_void_p), d.ctypes.data_as(C.c_void_p),
+                           len(s), _hip_stream(stream)), "page_copy")
+
+
+def page_save(cache: KVCache, ids, host_k, host_v, stream=None) -> None:
+    """Copy whole pages to host tensors (page ids[i] at row i of each)."""
+    a = _ids(ids)
+    cc = cache.c()
+    _check(lib().page_save(C.byref(cc), a.ctypes.data_as(C.c_void_p), len(a), _ptr(host_k),
+                           _ptr(host_v), _hip_stream(stream)), "page_save")
+
+
+def page_restore(cache: KVCache, ids, host_k, host_v, stream=None) -> None:
+    """Copy host tensors (row i -> page ids[i]) back into the pool."""
+    a = _ids(ids)
+    cc = cache.c()
+    _check(lib().page_restore(C.byref(cc), a.ctypes.data_as(C.c_void_p), len(a), _ptr(host_k),
+                              _ptr(host_v), _hip_stream(stream)), "page_restore")
 
 
 def page_pool_create(n_pages: int) -> PagePool:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -201,10 +202,11 @@ int32_t col_tiles_of(const pa_stream* s, const std::vector<int32_t>& grp, int32_
 
 // ---------------------------------------------------------------------------
 
+// Host bookkeeping of a page pool: one reference count per page id (0 free).
 struct pa_page_pool {
   int32_t n_pages;
   int32_t n_free;
-  std::vector<uint8_t> used;
+  std::vector<int32_t> refs;
 };
 
 extern "C" {
@@ -231,7 +233,7 @@ int page_pool_create(int32_t n_pages, pa_page_pool** out) {
   pa_page_pool* p = new (std::nothrow) pa_page_pool;
   if (!p) return PA_EINVAL;
   try {
-    p->used.assign((size_t)n_pages, 0);
+    p->refs.assign((size_t)n_pages, 0);
   } catch (...) {
     delete p;
     return PA_EINVAL;
@@ -250,28 +252,157 @@ int page_pool_alloc(pa_page_pool* pool, int32_t n, int32_t* ids_out) {
   if (n > pool->n_free) return PA_ENOSPC;
   int32_t k = 0;
   for (int32_t id = 0; id < pool->n_pages && k < n; ++id)
-    if (!pool->used[id]) {
-      pool->used[id] = 1;
+    if (pool->refs[id] == 0) {
+      pool->refs[id] = 1;
       ids_out[k++] = id;
     }
   pool->n_free -= k;
   return PA_OK;
 }
 
-int page_pool_free(pa_page_pool* pool, const int32_t* ids, int32_t n) {
-  if (!pool || n < 0 || (n > 0 && !ids)) return PA_EINVAL;
+namespace {
+// Occurrences of each id in ids[0..n), all in [0, n_pages), else empty.
+bool count_ids(const pa_page_pool* pool, const int32_t* ids, int32_t n,
+               std::vector<std::pair<int32_t, int32_t>>& counts) {
   std::vector<int32_t> v(ids, ids + n);
   std::sort(v.begin(), v.end());
-  for (int32_t i = 0; i < n; ++i) {
-    if (v[i] < 0 || v[i] >= pool->n_pages || !pool->used[v[i]]) return PA_ERANGE;
-    if (i > 0 && v[i] == v[i - 1]) return PA_ERANGE;
+  counts.clear();
+  for (int32_t id : v) {
+    if (id < 0 || id >= pool->n_pages) return false;
+    if (!counts.empty() && counts.back().first == id) ++counts.back().second;
+    else counts.emplace_back(id, 1);
   }
-  for (int32_t id : v) pool->used[id] = 0;
-  pool->n_free += n;
+  return true;
+}
+}  // namespace
+
+int page_pool_share(pa_page_pool* pool, const int32_t* ids, int32_t n) {
+  if (!pool || n < 0 || (n > 0 && !ids)) return PA_EINVAL;
+  std::vector<std::pair<int32_t, int32_t>> counts;
+  if (!count_ids(pool, ids, n, counts)) return PA_ERANGE;
+  for (const auto& c : counts)
+    if (pool->refs[c.first] == 0 || pool->refs[c.first] > INT32_MAX - c.second) return PA_ERANGE;
+  for (const auto& c : counts) pool->refs[c.first] += c.second;
   return PA_OK;
 }
 
+int page_pool_free(pa_page_pool* pool, const int32_t* ids, int32_t n) {
+  if (!pool || n < 0 || (n > 0 && !ids)) return PA_EINVAL;
+  std::vector<std::pair<int32_t, int32_t>> counts;
+  if (!count_ids(pool, ids, n, counts)) return PA_ERANGE;
+  for (const auto& c : counts)
+    if (pool->refs[c.first] < c.second) return PA_ERANGE;
+  for (const auto& c : counts) {
+    pool->refs[c.first] -= c.second;
+    if (pool->refs[c.first] == 0) ++pool->n_free;
+  }
+  return PA_OK;
+}
+
+int32_t page_pool_refcount(const pa_page_pool* pool, int32_t id) {
+  if (!pool) return PA_EINVAL;
+  if (id < 0 || id >= pool->n_pages) return PA_ERANGE;
+  return pool->refs[id];
+}
+
 int32_t page_pool_free_count(const pa_page_pool* pool) { return pool ? pool->n_free : PA_EINVAL; }
+
+// ---------------------------------------------------------------------------
+// Whole pages.
+
+}  // extern "C"
+
+namespace {
+
+int64_t page_bytes_of(const pa_kv_cache* c) {
+  return c->page_stride * (c->dtype == PA_KV_FP8_E4M3 ? 1 : 2);
+}
+
+// Checks shared by the page copies: a usable pool and ids in range.
+int check_pages(const pa_kv_cache* c, const int32_t* ids, int32_t n) {
+  if (!c || n < 0 || (n > 0 && !ids)) return PA_EINVAL;
+  if (c->dtype != PA_KV_BF16 && c->dtype != PA_KV_FP8_E4M3) return PA_EINVAL;
+  if (n == 0) return PA_OK;
+  if (!c->k_pages || !c->v_pages || c->n_pages < 1 || c->page_stride < 1) return PA_EINVAL;
+  if (page_bytes_of(c) % 16 != 0) return PA_EINVAL;
+  for (int32_t i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= c->n_pages) return PA_ERANGE;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int page_copy(const pa_kv_cache* cache, const int32_t* src_ids, const int32_t* dst_ids,
+              int32_t n, void* hip_stream) {
+  int rc = check_pages(cache, src_ids, n);
+  if (rc != PA_OK) return rc;
+  rc = check_pages(cache, dst_ids, n);
+  if (rc != PA_OK || n == 0) return rc;
+  std::vector<int32_t> d(dst_ids, dst_ids + n), sv(src_ids, src_ids + n);
+  std::sort(d.begin(), d.end());
+  std::sort(sv.begin(), sv.end());
+  for (int32_t i = 1; i < n; ++i)
+    if (d[i] == d[i - 1]) return PA_ERANGE;  // two copies onto one page
+  for (int32_t x : d)
+    if (std::binary_search(sv.begin(), sv.end(), x)) return PA_ERANGE;  // order would matter
+  for (int32_t at = 0; at < n; at += pa::kMaxCopyPairs) {
+    pa::PageCopyArgs A;
+    std::memset(&A, 0, sizeof A);
+    A.k = static_cast<uint8_t*>(cache->k_pages);
+    A.v = static_cast<uint8_t*>(cache->v_pages);
+    A.page_bytes = page_bytes_of(cache);
+    A.n_pairs = std::min<int32_t>(pa::kMaxCopyPairs, n - at);
+    for (int32_t i = 0; i < A.n_pairs; ++i) {
+      A.src[i] = src_ids[at + i];
+      A.dst[i] = dst_ids[at + i];
+    }
+    rc = pa::launch_page_copy(A, (hipStream_t)hip_stream);
+    if (rc != 0) return rc;
+  }
+  return PA_OK;
+}
+
+int page_save(const pa_kv_cache* cache, const int32_t* ids, int32_t n, void* host_k,
+              void* host_v, void* hip_stream) {
+  int rc = check_pages(cache, ids, n);
+  if (rc != PA_OK || n == 0) return rc;
+  if (!host_k || !host_v) return PA_EINVAL;
+  const int64_t P = page_bytes_of(cache);
+  for (int32_t i = 0; i < n; ++i) {
+    const uint8_t* k = static_cast<const uint8_t*>(cache->k_pages) + (int64_t)ids[i] * P;
+    const uint8_t* v = static_cast<const uint8_t*>(cache->v_pages) + (int64_t)ids[i] * P;
+    if (hipMemcpyAsync(static_cast<uint8_t*>(host_k) + i * P, k, (size_t)P,
+                       hipMemcpyDeviceToHost, (hipStream_t)hip_stream) != hipSuccess ||
+        hipMemcpyAsync(static_cast<uint8_t*>(host_v) + i * P, v, (size_t)P,
+                       hipMemcpyDeviceToHost, (hipStream_t)hip_stream) != hipSuccess)
+      return PA_EDEVICE;
+  }
+  return PA_OK;
+}
+
+int page_restore(const pa_kv_cache* cache, const int32_t* ids, int32_t n, const void* host_k,
+                 const void* host_v, void* hip_stream) {
+  int rc = check_pages(cache, ids, n);
+  if (rc != PA_OK || n == 0) return rc;
+  if (!host_k || !host_v) return PA_EINVAL;
+  std::vector<int32_t> d(ids, ids + n);
+  std::sort(d.begin(), d.end());
+  for (int32_t i = 1; i < n; ++i)
+    if (d[i] == d[i - 1]) return PA_ERANGE;  // two restores onto one page
+  const int64_t P = page_bytes_of(cache);
+  for (int32_t i = 0; i < n; ++i) {
+    uint8_t* k = static_cast<uint8_t*>(cache->k_pages) + (int64_t)ids[i] * P;
+    uint8_t* v = static_cast<uint8_t*>(cache->v_pages) + (int64_t)ids[i] * P;
+    if (hipMemcpyAsync(k, static_cast<const uint8_t*>(host_k) + i * P, (size_t)P,
+                       hipMemcpyHostToDevice, (hipStream_t)hip_stream) != hipSuccess ||
+        hipMemcpyAsync(v, static_cast<const uint8_t*>(host_v) + i * P, (size_t)P,
+                       hipMemcpyHostToDevice, (hipStream_t)hip_stream) != hipSuccess)
+      return PA_EDEVICE;
+  }
+  return PA_OK;
+}
 
 // ---------------------------------------------------------------------------
 

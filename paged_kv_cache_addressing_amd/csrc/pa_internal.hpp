@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "pa_kargs.hpp"
 
 namespace pa {
@@ -17,5 +19,6 @@ int prefill_columns(int head_dim);
 int prefill_wg_columns(int head_dim);
 int launch_prefill(const PrefillArgs& A, int kv_dtype, int head_dim, hipStream_t st);
 int launch_write_kv(const WriteArgs& A, int kv_dtype, int head_dim, hipStream_t st);
+int launch_page_copy(const PageCopyArgs& A, hipStream_t st);
 
 }  // namespace pa

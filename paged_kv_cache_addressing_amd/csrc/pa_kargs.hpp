@@ -95,4 +95,16 @@ struct WriteArgs {
   StreamArg s[kMaxLaunchStreams];
 };
 
+constexpr int kMaxCopyPairs = 128;  // page pairs per copy launch; calls are chunked
+
+struct PageCopyArgs {
+  uint8_t* k;           // pool K base
+  uint8_t* v;           // pool V base
+  int64_t page_bytes;   // page_stride * element size (multiple of 16)
+  int32_t n_pairs;
+  int32_t pad0;
+  int32_t src[kMaxCopyPairs];
+  int32_t dst[kMaxCopyPairs];
+};
+
 }  // namespace pa

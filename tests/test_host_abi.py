@@ -89,6 +89,50 @@ def test_pool_free_rejects_bad_ids_atomically():
     assert pool.free_count() == 4
 
 
+def test_pool_shared_pages_count_references():
+    pool = pa.PagePool(6)
+    prefix = pool.alloc(3)              # stream A's pages
+    assert [pool.refcount(i) for i in range(6)] == [1, 1, 1, 0, 0, 0]
+    pool.share(prefix[:2])              # stream B reuses A's first two pages
+    pool.share([prefix[0]])             # and stream C the first
+    assert [pool.refcount(i) for i in prefix] == [3, 2, 1]
+    pool.free(prefix)                   # A finishes: only its own third page is freed
+    assert pool.free_count() == 4 and pool.refcount(prefix[2]) == 0
+    assert list(pool.alloc(1)) == [2]   # lowest free id first
+    pool.free([prefix[0], prefix[0]])   # two references dropped in one call
+    assert pool.refcount(prefix[0]) == 0 and pool.refcount(prefix[1]) == 1
+    for bad, status in (([prefix[1], prefix[1]], pa.PA_ERANGE),  # more than it holds
+                        ([5], pa.PA_ERANGE), ([9], pa.PA_ERANGE)):
+        with pytest.raises(pa.PagedAttnError) as e:
+            pool.free(bad)
+        assert e.value.status == status
+    with pytest.raises(pa.PagedAttnError) as e:
+        pool.share([4])                 # a free page cannot be shared
+    assert e.value.status == pa.PA_ERANGE
+    assert pool.refcount(prefix[1]) == 1  # the failed calls changed nothing
+    with pytest.raises(pa.PagedAttnError):
+        pool.refcount(6)
+
+
+def test_page_copy_save_restore_validation():
+    c = cache()
+    ids = (C.c_int32 * 2)(0, 1)
+    far = (C.c_int32 * 2)(0, 64)
+    same = (C.c_int32 * 2)(2, 2)
+    L = pa.lib()
+    assert L.page_copy(None, ids, ids, 2, None) == pa.PA_EINVAL
+    assert L.page_copy(C.byref(c), ids, far, 2, None) == pa.PA_ERANGE       # page 64 of 64
+    assert L.page_copy(C.byref(c), ids, same, 2, None) == pa.PA_ERANGE      # two onto one
+    assert L.page_copy(C.byref(c), ids, (C.c_int32 * 2)(1, 3), 2, None) == pa.PA_ERANGE  # dst is a src
+    assert L.page_copy(C.byref(c), ids, ids, 0, None) == pa.PA_OK
+    odd = cache(page_stride=4 * 256 * 256 + 1)  # not a multiple of 16 bytes
+    assert L.page_copy(C.byref(odd), ids, (C.c_int32 * 2)(2, 3), 2, None) == pa.PA_EINVAL
+    assert L.page_save(C.byref(c), far, 2, FAKE, FAKE, None) == pa.PA_ERANGE
+    assert L.page_save(C.byref(c), ids, 2, None, FAKE, None) == pa.PA_EINVAL
+    assert L.page_restore(C.byref(c), same, 2, FAKE, FAKE, None) == pa.PA_ERANGE
+    assert L.page_restore(C.byref(c), ids, 2, FAKE, None, None) == pa.PA_EINVAL
+
+
 def test_pool_create_rejects_empty():
     h = C.c_void_p()
     assert pa.lib().page_pool_create(0, C.byref(h)) == pa.PA_EINVAL
