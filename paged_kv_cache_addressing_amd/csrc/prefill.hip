@@ -2,27 +2,31 @@
 //
 // The prompt rows read the cache through the page table, with the page size
 // a compile-time constant of 256 and one page lookup per page (TensorFold
-// pull request #1373, prompt rows; pull request #2011, hpattn_p256_kernel and
-// "a paged item's page looked up once").  Keys past a row's limit land as
-// zeros (pull request #2011 review, "Is paged output the same as windowed
+// pull request #1373, prompt rows; pull request #2011, the 256-position
+// prompt kernel and the commit that looks a paged item's page up once
+// instead of per 16-byte chunk).  Keys past a row's limit contribute zeros
+// (pull request #2011 review, "Is paged output the same as windowed
 // output?").
 //
-// Work split.  A workgroup (4 waves) owns one kv head, HW of its q heads and
-// a tile of query rows; each wave owns 16*NT MFMA columns, a column being one
-// (row, q head) pair: NT = 2 at head_dim 256 (16 rows x 2 heads for a group of
-// 6), NT = 3 at 128.  The K/V tiles in LDS serve all HW heads, and the other
-// head groups of the same kv head run on the same XCD, so K/V also hit in L2.
-//
-// Split mode (decode streams with many rows, e.g. speculative verify rows):
-// the same kernel computes one 4,096-key split (any split_keys) of a row
-// tile covering the whole group (16 rows x 6 heads = 96 columns in three
-// waves), so each split's K/V is read from HBM once for all its columns, and
-// writes the split's (m, l, o) partial for the log-sum-exp merge (TensorFold
-// issue #1344, "Mechanism").
+// Work split.  A workgroup owns one kv head, HW of its q heads and a tile of
+// query rows; its NW waves own 16*NT MFMA columns each, a column being one
+// (row, q head) pair (column c of the workgroup is (c / HW, c % HW)).  At
+// head_dim 256: 8 waves of one n-tile (two waves per SIMD); at 128: 4 waves
+// of three.  The K/V tiles in LDS serve all HW heads, and the other head
+// groups of the same kv head run on the same XCD, so K/V also hit in L2.
 //   S^T (32 keys x 16NT cols) = K Q^T    : 2 m-tiles x NT n-tiles x D/32 k-steps
 //   O^T (D x 16NT cols)      += V^T P^T  : D/16 m-tiles x NT n-tiles x 1 k-step
 // The key order inside a step is permuted so each lane's S^T C-rows are the
 // 8 consecutive keys of its P^T operand (no shuffles between the products).
+//
+// Split mode (decode streams with many rows, e.g. speculative verify rows):
+// the same kernel computes one split_keys-key split of a row tile covering
+// the whole group (16 rows x 6 heads = 96 columns), so each split's K/V is
+// read from HBM once for all its columns, and writes the split's (m, l, o)
+// partial for the log-sum-exp merge (TensorFold issue #1344, "Mechanism").
+// Rows may carry an ancestor table (draft trees; pull request #1355,
+// follow-up checks, "Indexing"): then, of the rows' own keys, a row sees
+// only those its word marks.
 //
 // Pipeline.  K and V steps (32 keys) rotate through three LDS slots each, in
 // "fragment order" (the 1 KiB an MFMA operand needs is contiguous, lane l's
