@@ -28,10 +28,10 @@
 // follow-up checks, "Indexing"): then, of the rows' own keys, a row sees
 // only those its word marks.
 //
-// Pipeline.  K and V steps (32 keys) rotate through three LDS slots each, in
-// "fragment order" (the 1 KiB an MFMA operand needs is contiguous, lane l's
-// 16 bytes at l*16, so ds_read_b128 is conflict-free).  bf16 arrives by
-// global_load_lds_dwordx4 straight into LDS, two steps ahead; fp8 codes
+// Pipeline.  K and V steps (32 keys) rotate through three K and four V LDS
+// slots, in "fragment order" (the 1 KiB an MFMA operand needs is contiguous,
+// lane l's 16 bytes at l*16, so ds_read_b128 is conflict-free).  bf16 arrives
+// by buffer_load_dwordx4 ... lds straight into LDS, two steps ahead; fp8 codes
 // arrive the same way into a staging ring three steps ahead and are
 // converted to bf16 fragment order once, one step ahead.  In step v
 // a wave computes S(v+1) = K(v+1) Q^T on the matrix cores while the VALU does
@@ -71,6 +71,21 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// LDS-DMA through a buffer resource spanning one page tile: each lane's 16
+// bytes at voff + soff land at lds_dst + 16 * lane.  The buffer form is used
+// rather than the global one because the compiler counts a global LDS-DMA as
+// a flat access that may retire out of order with LDS reads; while one is in
+// flight it then waits for every LDS read with lgkmcnt(0), which undoes the
+// fragment read-ahead.  Offsets past the tile read zeros.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  // dword 3: 32-bit data format (required for untyped access), no swizzle
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, int voff, int soff, v4u* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+}
+
 template <int KV, int D>
 __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const PrefillArgs A) {
   // A workgroup owns one kv head g, HW = heads_per_wg of its q heads (head
@@ -88,7 +103,8 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   constexpr int VF = MD;                // V fragments per step
   constexpr int KPW = KF / NW;          // DMA fragments per wave per step
   constexpr int VPW = VF / NW;
-  constexpr int NSLOT = 3;
+  constexpr int NSLOT = 3;              // K slots
+  constexpr int NVSLOT = 4;             // V slots (see the step schedule)
   constexpr int KSLOT = KF * 64;        // 16-byte entries per slot
   constexpr int VSLOT = VF * 64;
   // fp8: raw codes land in a staging ring (16-byte entries per step) and are
@@ -100,7 +116,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   constexpr int V8PW = VST / NTH;
   static_assert(kPage % BK == 0, "a step never straddles two pages");
 
-  __shared__ v4u lds[NSLOT * (KSLOT + VSLOT) + (KV ? NSTG * (KST + VST) : 0)];
+  __shared__ v4u lds[NSLOT * KSLOT + NVSLOT * VSLOT + (KV ? NSTG * (KST + VST) : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -213,23 +229,25 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   // on the step (loop invariant, hoisted into VGPRs).
   auto dma_k = [&](int v, int sl) {
     const PageTile& T = page_k(v);
-    const uint8_t* base = T.k + (int64_t)(v & 7) * BK * D * 2;
+    const auto rs = tile_rsrc(T.k, kPage * D * 2);
+    const int soff = (v & 7) * BK * D * 2;
     v4u* dst = Kbase + sl * KSLOT + wave * KPW * 64;
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
       const int f = wave * KPW + i, mt = f / KS, ks = f % KS;
       const int off = ((krow + 4 * mt) * D + 32 * ks + 8 * a) * 2;
-      __builtin_amdgcn_global_load_lds(base + off, dst + i * 64, 16, 0, 0);
+      dma16(rs, off, soff, dst + i * 64);
     }
   };
   auto dma_v = [&](int v, int sl) {
     const PageTile& T = page_v(v);
-    const uint8_t* base = T.v + (int64_t)(v & 7) * BK * D * 2;
+    const auto rs = tile_rsrc(T.v, kPage * D * 2);
+    const int soff = (v & 7) * BK * D * 2;
     v4u* dst = Vbase + sl * VSLOT + wave * VPW * 64;
 #pragma unroll
     for (int i = 0; i < VPW; ++i) {
       const int off = v_off<D, ESZ>(8 * a, 16 * (wave * VPW + i) + n) * 2;
-      __builtin_amdgcn_global_load_lds(base + off, dst + i * 64, 16, 0, 0);
+      dma16(rs, off, soff, dst + i * 64);
     }
   };
   // bf16 tail: values at or past n_keys_t in a landed V step become zeros.
@@ -247,34 +265,34 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   // converts it; the conversion to bf16 fragment order then runs one step
   // ahead of use (K two steps).  Every E4M3FN value is a bf16 value, so the
   // conversion is exact.
-  v4u* const Sbase = lds + NSLOT * (KSLOT + VSLOT);
+  v4u* const Sbase = lds + NSLOT * KSLOT + NVSLOT * VSLOT;
   auto dma8_k = [&](int v, int sl) {
     const PageTile& T = page_k(v);
-    const uint8_t* base = T.k + (int64_t)(v & 7) * BK * D;
+    const auto rs = tile_rsrc(T.k, kPage * D);
+    const int soff = (v & 7) * BK * D;
     v4u* dst = Sbase + sl * (KST + VST);
 #pragma unroll
     for (int i = 0; i < K8PW; ++i) {
       // entry fp*64 + lane: 16 dims (two QK k-steps) of one S^T row
       const int fp = NW * i + wave, mt = fp / (KS / 2), kq = fp % (KS / 2);
       const int off = (krow + 4 * mt) * D + 64 * kq + 16 * a;
-      __builtin_amdgcn_global_load_lds(base + off, dst + fp * 64, 16, 0, 0);
+      dma16(rs, off, soff, dst + fp * 64);
     }
   };
   auto dma8_v = [&](int v, int sl) {
     const PageTile& T = page_v(v);
     const int o = (v & 7) * BK;
+    const auto rs = tile_rsrc(T.v, kPage * D);
     v4u* dst = Sbase + sl * (KST + VST) + KST;
 #pragma unroll
     for (int i = 0; i < V8PW; ++i) {
       // entry q: 16 keys (half h of the step) of dim 16*md + dl
-      // (the offset is named first: a call nested in the builtin's argument
-      // list makes the host pass drop the kernel's launch stub)
       const int q = i * NTH + tid, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
       const int off = v_off<D, ESZ>(o + 16 * h, 16 * md + dl);
-      __builtin_amdgcn_global_load_lds(T.v + off, dst + (q >> 6) * 64, 16, 0, 0);
+      dma16(rs, off, 0, dst + (q >> 6) * 64);
     }
   };
-  auto convert_fp8 = [&](int vk, int slk, int vv, int slv, auto may_tail) {
+  auto convert_fp8 = [&](int vk, int slk, int vv, int stv, int slv, auto may_tail) {
     if (vk >= 0) {
       const v4u* St = Sbase + slk * (KST + VST);
       v4u* Ls = Kbase + slk * KSLOT;
@@ -288,7 +306,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       }
     }
     if (vv >= 0) {
-      const v4u* St = Sbase + slv * (KST + VST) + KST;
+      const v4u* St = Sbase + stv * (KST + VST) + KST;
       v4u* Ls = Vbase + slv * VSLOT;
       const bool tail = decltype(may_tail)::value && vv * BK + BK > n_keys_t;
 #pragma unroll
@@ -446,30 +464,69 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
 
   // One step: issue the loads two (bf16) or one (fp8) steps ahead; S(v+1)
   // on the matrix cores alongside softmax(v) on the VALU; O += V(v) P(v);
-  // then wait for the next step's tiles and release this step's slots.
+  // and the hand-off: wait for the next steps' tiles, then a barrier that
+  // publishes them and releases the slots read before it.
   // FAST is the steady state (every prefetch in range, no causal mask, no
-  // key-range tail), where the step runs without any of those checks.  LDS
-  // slots (and fp8 staging entries) rotate with the step: step v uses ring
-  // position (v - v_lo) % 3, passed in as `ph` (a compile-time constant in
-  // the unrolled steady state).
-  static_assert(NSLOT == 3 && NSTG == 3, "one ring period for slots and staging");
+  // key-range tail), where the step runs without any of those checks.  K
+  // slots and fp8 staging entries rotate with the step through three ring
+  // positions, (v - v_lo) % 3, passed in as `ph` (a compile-time constant in
+  // the unrolled steady state); V slots rotate through four.
+  //
+  // Staggered waves.  With two waves per SIMD, the second wave of each SIMD
+  // (`lag`) takes the hand-off between its S product and its P.V product,
+  // the first after its P.V product.  Between two barriers one wave of a
+  // SIMD then runs S(v+1) and the softmax (VALU work, K reads) while the
+  // other runs P.V (V reads), so neither the matrix cores nor the LDS idle
+  // in one phase and saturate in the other.  A lagging wave reads V(v-1)
+  // after barrier v-1, which is why V needs a fourth slot: V(v+2), DMAed
+  // after that barrier, may not reuse V(v-1)'s slot.  Every wave still
+  // passes one barrier per step, in the same order.
+  static_assert(NSLOT == 3 && NSTG == 3 && NVSLOT == 4, "ring periods");
+  const bool lag = NW == 8 && wave >= NW / 2;
   auto step = [&](int v, v4f (&Sc)[MT][NT], v4f (&Sn)[MT][NT], auto fast, auto ph) {
     constexpr bool FAST = decltype(fast)::value;
     const int r0 = ph % 3, r1 = (ph + 1) % 3, r2 = (ph + 2) % 3;  // v, v+1 (and v+4), v+2
+    const int q0 = (v - v_lo) & 3, q1 = (v + 1 - v_lo) & 3, q2 = (v + 2 - v_lo) & 3;
     int issued = 0;
     if (KV == 0) {
-      if (FAST || v + 2 < v_hi) { dma_v(v + 2, r2); issued = 1; }
+      if (FAST || v + 2 < v_hi) { dma_v(v + 2, q2); issued = 1; }
       if (FAST || v + 3 < v_hi) { dma_k(v + 3, r0); issued = 2; }
     } else {
       if (FAST || v + 4 < v_hi) dma8_k(v + 4, r1);
       if (FAST || v + 3 < v_hi) dma8_v(v + 3, r0);
     }
+    auto hand_off = [&]() {
+      if (KV == 0) {
+        if (FAST || issued == 2) wait_vmem<KPW + VPW>();
+        else if (issued == 1) wait_vmem<VPW>();
+        else wait_vmem<0>();
+      } else {
+        // K(v+2) and V(v+1) have landed once at most the DMAs issued in steps
+        // v-1 and v (K(v+3), V(v+2), K(v+4), V(v+3), those that exist) remain.
+        const int r = v_hi - 1 - v;
+        if (FAST || r >= 4) wait_vmem<2 * (K8PW + V8PW)>();
+        else if (r == 3) wait_vmem<K8PW + 2 * V8PW>();
+        else if (r == 2) wait_vmem<V8PW>();
+        else wait_vmem<0>();
+        if (FAST) convert_fp8(v + 2, r2, v + 1, r1, q1, std::false_type{});
+        else convert_fp8(v + 2 < v_hi ? v + 2 : -1, r2, v + 1 < v_hi ? v + 1 : -1, r1, q1,
+                         std::true_type{});
+      }
+      lds_barrier();
+      if (!FAST && KV == 0 && v + 1 < v_hi && (v + 1) * BK + BK > n_keys_t) {
+        zero_tail_bf16(v + 1, q1);
+        lds_barrier();
+      }
+    };
+    v8bf P[NT];
+    float alpha[NT];
     if (wave_active) {
       if (!FAST && v * BK + BK - 1 >= mask_from) mask(v, Sc);
-      v8bf P[NT];
-      float alpha[NT];
       // K(v+1), or stale data past the end (unused)
       qk_softmax(r1 * KSLOT, Sn, Sc, P, alpha);
+    }
+    if (lag) hand_off();
+    if (wave_active) {
       bool moved = false;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) moved |= alpha[nt] != 1.f;
@@ -479,29 +536,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) o[md][nt] *= alpha[nt];
       }
-      pv(r0 * VSLOT, P);
+      pv(q0 * VSLOT, P);
     }
-    if (KV == 0) {
-      if (FAST || issued == 2) wait_vmem<KPW + VPW>();
-      else if (issued == 1) wait_vmem<VPW>();
-      else wait_vmem<0>();
-    } else {
-      // K(v+2) and V(v+1) have landed once at most the DMAs issued in steps
-      // v-1 and v (K(v+3), V(v+2), K(v+4), V(v+3), those that exist) remain.
-      const int r = v_hi - 1 - v;
-      if (FAST || r >= 4) wait_vmem<2 * (K8PW + V8PW)>();
-      else if (r == 3) wait_vmem<K8PW + 2 * V8PW>();
-      else if (r == 2) wait_vmem<V8PW>();
-      else wait_vmem<0>();
-      if (FAST) convert_fp8(v + 2, r2, v + 1, r1, std::false_type{});
-      else convert_fp8(v + 2 < v_hi ? v + 2 : -1, r2, v + 1 < v_hi ? v + 1 : -1, r1,
-                       std::true_type{});
-    }
-    lds_barrier();
-    if (!FAST && KV == 0 && v + 1 < v_hi && (v + 1) * BK + BK > n_keys_t) {
-      zero_tail_bf16(v + 1, r1);
-      lds_barrier();
-    }
+    if (!lag) hand_off();
   };
 
   // Prologue: K(v_lo), V(v_lo), K(v_lo+1) resident as bf16 (bf16 also has
@@ -525,8 +562,8 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       dma8_v(v_lo, 0);
       if (n_st > 1) dma8_k(v_lo + 1, 1);
       wait_vmem<0>();
-      convert_fp8(v_lo, 0, v_lo, 0, std::true_type{});
-      if (n_st > 1) convert_fp8(v_lo + 1, 1, -1, 0, std::true_type{});
+      convert_fp8(v_lo, 0, v_lo, 0, 0, std::true_type{});
+      if (n_st > 1) convert_fp8(v_lo + 1, 1, -1, 0, 0, std::true_type{});
       // the staging reads above finish before K(v_lo+3) reuses K(v_lo)'s entries
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (n_st > 1) dma8_v(v_lo + 1, 1);
