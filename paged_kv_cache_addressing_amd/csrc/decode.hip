@@ -33,7 +33,7 @@ __device__ __forceinline__ int qk_d(int ks, int a) {
 }
 
 template <int KV, int D>
-__global__ __launch_bounds__(256, 2) void decode_partial_kernel(const DecodeArgs A) {
+__global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs A) {
   constexpr int ESZ = KV ? 1 : 2;
   constexpr int KK = KV ? 2 : 1;      // 32-key PV k-steps per chunk
   constexpr int CK = 32 * KK;         // keys per chunk
@@ -98,108 +98,152 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(const DecodeArgs
   // S^T row m of m-tile mt holds key 8*KK*(m/4) + 4*mt + m%4 of the chunk.
   const int krow = 8 * KK * (n >> 2) + (n & 3);
 
-  for (int p = p_lo + wave; p < p_hi; p += NW) {
-    const PageTile T = page_tile<D, ESZ>(S, A.cache, p, g);
-    bad |= !T.ok;
-    const int key_end = min(kPage, k_hi - p * kPage);
-    for (int c0 = 0; c0 < key_end; c0 += CK) {
-      v4u kr[KL], vr[MD];
+  // The wave's chunks, in order: its pages p_lo + wave, + NW, ..., each cut
+  // into CK-key chunks up to the split's end.  Two register sets alternate:
+  // the next chunk's K and V loads are issued before this chunk's products,
+  // so a wave always has a chunk of bytes in flight while it computes.
+  auto load = [&](v4u (&kr)[KL], v4u (&vr)[MD], const PageTile& T, int c0) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint8_t* kp = T.k + (int64_t)(c0 + krow + 4 * mt) * D * ESZ;
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint8_t* kp = T.k + (int64_t)(c0 + krow + 4 * mt) * D * ESZ;
+      if (KV) {
+#pragma unroll
+        for (int kq = 0; kq < KS / 2; ++kq) kr[mt * (KS / 2) + kq] = load16(kp + 64 * kq + 16 * a);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kr[mt * KS + ks] = load16(kp + (32 * ks + 8 * a) * 2);
+      }
+    }
+    // V block of this chunk (CK == 64/ESZ keys): D rows of 64 bytes.
+    const uint8_t* vb = T.v + (int64_t)c0 * D * ESZ + (8 * KK * a) * ESZ;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) vr[md] = load16(vb + (16 * md + n) * 64);
+  };
+  auto chunk = [&](v4u (&kr)[KL], v4u (&vr)[MD], int p, int c0) {
+    v4f sacc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      sacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        v8bf ka;
         if (KV) {
-#pragma unroll
-          for (int kq = 0; kq < KS / 2; ++kq) kr[mt * (KS / 2) + kq] = load16(kp + 64 * kq + 16 * a);
+          const v4u x = kr[mt * (KS / 2) + (ks >> 1)];
+          ka = (ks & 1) ? fp8x8_to_bf16(x[2], x[3]) : fp8x8_to_bf16(x[0], x[1]);
         } else {
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) kr[mt * KS + ks] = load16(kp + (32 * ks + 8 * a) * 2);
+          ka = as_bf(kr[mt * KS + ks]);
         }
+        sacc[mt] = mfma16(ka, qb[ks], sacc[mt]);
       }
-      // V block of this chunk (CK == 64/ESZ keys): D rows of 64 bytes.
-      const uint8_t* vb = T.v + (int64_t)c0 * D * ESZ + (8 * KK * a) * ESZ;
-#pragma unroll
-      for (int md = 0; md < MD; ++md) vr[md] = load16(vb + (16 * md + n) * 64);
+    }
 
-      v4f sacc[MT];
+    // Online softmax for this lane's column over its 4*MT keys.
+    const int kabs0 = p * kPage + c0 + 8 * KK * a;
+    const bool need_mask = p * kPage + c0 + CK - 1 >= mask_from;
+    float sv[MT][4];
+    float mx = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        sacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          v8bf ka;
-          if (KV) {
-            const v4u x = kr[mt * (KS / 2) + (ks >> 1)];
-            ka = (ks & 1) ? fp8x8_to_bf16(x[2], x[3]) : fp8x8_to_bf16(x[0], x[1]);
-          } else {
-            ka = as_bf(kr[mt * KS + ks]);
-          }
-          sacc[mt] = mfma16(ka, qb[ks], sacc[mt]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        float v = sacc[mt][i] * A.scale_log2;
+        const int kabs = kabs0 + 4 * mt + i, rel = kabs - S.first_pos;
+        const bool vis = (kabs <= pos) & ((rel < 0) | (((anc >> (rel & 31)) & 1u) != 0u));
+        if (need_mask && !vis) v = -INFINITY;
+        sv[mt][i] = v;
+        mx = fmaxf(mx, v);
       }
+    mx = rows4_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[mt][i] = __builtin_amdgcn_exp2f(sv[mt][i] - m_use);
+        psum += sv[mt][i];
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md) o[md] *= alpha;
+    }
+    v8bf pb[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      v4u x;
+      x[0] = pack_bf2(sv[2 * kk][0], sv[2 * kk][1]);
+      x[1] = pack_bf2(sv[2 * kk][2], sv[2 * kk][3]);
+      x[2] = pack_bf2(sv[2 * kk + 1][0], sv[2 * kk + 1][1]);
+      x[3] = pack_bf2(sv[2 * kk + 1][2], sv[2 * kk + 1][3]);
+      pb[kk] = as_bf(x);
+    }
 
-      // Online softmax for this lane's column over its 4*MT keys.
-      const int kabs0 = p * kPage + c0 + 8 * KK * a;
-      const bool need_mask = p * kPage + c0 + CK - 1 >= mask_from;
-      float sv[MT][4];
-      float mx = -INFINITY;
+    // Keys at or past n_keys may be unwritten: their values land as zeros.
+    if (p * kPage + c0 + CK > S.n_keys) {
+      const int nv = S.n_keys - kabs0;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int md = 0; md < MD; ++md) vr[md] = KV ? keep_first_b(vr[md], nv) : keep_first_h(vr[md], nv);
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[mt][i] * A.scale_log2;
-          const int kabs = kabs0 + 4 * mt + i, rel = kabs - S.first_pos;
-          const bool vis = (kabs <= pos) & ((rel < 0) | (((anc >> (rel & 31)) & 1u) != 0u));
-          if (need_mask && !vis) v = -INFINITY;
-          sv[mt][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = rows4_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[mt][i] = __builtin_amdgcn_exp2f(sv[mt][i] - m_use);
-          psum += sv[mt][i];
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int md = 0; md < MD; ++md) o[md] *= alpha;
-      }
-      v8bf pb[KK];
+    for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        v4u x;
-        x[0] = pack_bf2(sv[2 * kk][0], sv[2 * kk][1]);
-        x[1] = pack_bf2(sv[2 * kk][2], sv[2 * kk][3]);
-        x[2] = pack_bf2(sv[2 * kk + 1][0], sv[2 * kk + 1][1]);
-        x[3] = pack_bf2(sv[2 * kk + 1][2], sv[2 * kk + 1][3]);
-        pb[kk] = as_bf(x);
+        v8bf va;
+        if (KV)
+          va = kk ? fp8x8_to_bf16(vr[md][2], vr[md][3]) : fp8x8_to_bf16(vr[md][0], vr[md][1]);
+        else
+          va = as_bf(vr[md]);
+        o[md] = mfma16(va, pb[kk], o[md]);
       }
-
-      // Keys at or past n_keys may be unwritten: their values land as zeros.
-      if (p * kPage + c0 + CK > S.n_keys) {
-        const int nv = S.n_keys - kabs0;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) vr[md] = KV ? keep_first_b(vr[md], nv) : keep_first_h(vr[md], nv);
-      }
-#pragma unroll
-      for (int md = 0; md < MD; ++md)
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          v8bf va;
-          if (KV)
-            va = kk ? fp8x8_to_bf16(vr[md][2], vr[md][3]) : fp8x8_to_bf16(vr[md][0], vr[md][1]);
-          else
-            va = as_bf(vr[md]);
-          o[md] = mfma16(va, pb[kk], o[md]);
-        }
+  };
+  // (p, c0) -> the wave's next chunk
+  auto advance = [&](int& p, int& c0) {
+    c0 += CK;
+    if (c0 >= min(kPage, k_hi - p * kPage)) {
+      p += NW;
+      c0 = 0;
     }
+  };
+  v4u krA[KL], vrA[MD], krB[KL], vrB[MD];
+  int p = p_lo + wave, c0 = 0;
+  PageTile T{};
+  if (p < p_hi) {
+    T = page_tile<D, ESZ>(S, A.cache, p, g);
+    bad |= !T.ok;
+    load(krA, vrA, T, c0);
+  }
+  // Issue the loads of the chunk after (p, c0) into (kr, vr); returns it.
+  auto prefetch = [&](v4u (&kr)[KL], v4u (&vr)[MD], int& pn, int& cn, PageTile& Tn) {
+    pn = p;
+    cn = c0;
+    advance(pn, cn);
+    Tn = T;
+    if (pn < p_hi) {
+      if (pn != p) {
+        Tn = page_tile<D, ESZ>(S, A.cache, pn, g);
+        bad |= !Tn.ok;
+      }
+      load(kr, vr, Tn, cn);
+    }
+  };
+  while (p < p_hi) {
+    int pn, cn;
+    PageTile Tn;
+    prefetch(krB, vrB, pn, cn, Tn);
+    chunk(krA, vrA, p, c0);
+    p = pn;
+    c0 = cn;
+    T = Tn;
+    if (p >= p_hi) break;
+    prefetch(krA, vrA, pn, cn, Tn);
+    chunk(krB, vrB, p, c0);
+    p = pn;
+    c0 = cn;
+    T = Tn;
   }
 
   // Per-column row sum across the four lane groups, in a fixed order.
