@@ -298,20 +298,39 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs A) {
   const int ns = S.n_splits;
   const int64_t slot0 = S.slot_base + ((int64_t)r * A.n_q_heads + h) * ns;
   const float* ml = A.ws_ml + 2 * slot0;
+  // Loads are batched JB splits at a time so their latencies overlap; the
+  // sums still run in split order.
+  constexpr int JB = 8;
   float M = -INFINITY;
   bool bad = false;
-  for (int j = 0; j < ns; ++j) {
-    const float m = ml[2 * j];
-    bad |= m != m;
-    M = fmaxf(M, m);
+  for (int j0 = 0; j0 < ns; j0 += JB) {
+    float mb[JB];
+#pragma unroll
+    for (int u = 0; u < JB; ++u) mb[u] = j0 + u < ns ? ml[2 * (j0 + u)] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < JB; ++u) {
+      bad |= mb[u] != mb[u];
+      M = fmaxf(M, mb[u]);
+    }
   }
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float num = 0.f, den = 0.f;
-    for (int j = 0; j < ns; ++j) {
-      const float m = ml[2 * j];
-      const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      num += w * A.ws_o[(slot0 + j) * D + d];
-      den += w * ml[2 * j + 1];
+    for (int j0 = 0; j0 < ns; j0 += JB) {
+      float ob[JB], mb[JB], lb[JB];
+#pragma unroll
+      for (int u = 0; u < JB; ++u) {
+        const bool in = j0 + u < ns;
+        ob[u] = in ? A.ws_o[(slot0 + j0 + u) * D + d] : 0.f;
+        mb[u] = in ? ml[2 * (j0 + u)] : -INFINITY;
+        lb[u] = in ? ml[2 * (j0 + u) + 1] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < JB; ++u) {
+        if (j0 + u >= ns) break;
+        const float w = mb[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb[u] - M);
+        num += w * ob[u];
+        den += w * lb[u];
+      }
     }
     const float res = bad ? __builtin_nanf("") : num / den * A.v_scale;
     A.out[((int64_t)(S.row_offset + r) * A.n_q_heads + h) * D + d] = f2bf(res);
