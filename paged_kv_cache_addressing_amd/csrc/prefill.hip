@@ -522,8 +522,12 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
     float alpha[NT];
     if (wave_active) {
       if (!FAST && v * BK + BK - 1 >= mask_from) mask(v, Sc);
-      // K(v+1), or stale data past the end (unused)
+      // K(v+1), or stale data past the end (unused).  This phase (matrix
+      // products, softmax and K reads) is the longer one, so its wave takes
+      // issue priority over a P.V-phase wave on the same SIMD.
+      __builtin_amdgcn_s_setprio(1);
       qk_softmax(r1 * KSLOT, Sn, Sc, P, alpha);
+      __builtin_amdgcn_s_setprio(0);
     }
     if (lag) hand_off();
     if (wave_active) {
