@@ -160,19 +160,19 @@ struct RowTiling {
 // Prefill: the largest divisor of the group that also divides a wave's
 // column count, so no wave holds a partial row and the workgroup's K/V
 // tiles serve as many q heads as that allows.
-RowTiling prefill_tiling(int32_t head_dim, int32_t group) {
-  const int32_t cols = pa::prefill_columns(head_dim);
+RowTiling prefill_tiling(int32_t kv_dtype, int32_t head_dim, int32_t group) {
+  const int32_t cols = pa::prefill_columns(kv_dtype, head_dim);
   int32_t hw = 1;
   for (int32_t d = 1; d <= group && d <= cols; ++d)
     if (group % d == 0 && cols % d == 0) hw = d;
-  return {hw, pa::prefill_wg_columns(head_dim) / hw};
+  return {hw, pa::prefill_wg_columns(kv_dtype, head_dim) / hw};
 }
 
 // Decode streams with many columns: the largest divisor of the group that
 // fits the workgroup's columns (the whole group whenever it fits), so every
 // split's K/V is read by as few workgroups as possible.
-RowTiling wide_tiling(int32_t head_dim, int32_t group) {
-  const int32_t cols = pa::prefill_wg_columns(head_dim);
+RowTiling wide_tiling(int32_t kv_dtype, int32_t head_dim, int32_t group) {
+  const int32_t cols = pa::prefill_wg_columns(kv_dtype, head_dim);
   int32_t hw = 1;
   for (int32_t d = 1; d <= group && d <= cols; ++d)
     if (group % d == 0) hw = d;
@@ -462,7 +462,8 @@ int paged_attn_decode_plan(const pa_stream* streams, int32_t n_streams, int32_t 
   if (plan) {
     std::memset(plan, 0, sizeof *plan);
     const int32_t group = n_q_heads / n_kv_heads;
-    const RowTiling W = wide_tiling(head_dim, group);
+    // (a workgroup's column count does not depend on the KV dtype)
+    const RowTiling W = wide_tiling(PA_KV_BF16, head_dim, group);
     plan->n_launch_groups = (int32_t)P.groups.size();
     for (const auto& grp : P.groups) {
       int32_t tr = 0, narrow_splits = 0, wide_items = 0;
@@ -524,7 +525,7 @@ int prepare_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n
   const float ks = cache->dtype == PA_KV_FP8_E4M3 ? cache->k_scale : 1.f;
   const float scale_log2 = sm_scale * ks * kLog2e;
   const float vs = cache->dtype == PA_KV_FP8_E4M3 ? cache->v_scale : 1.f;
-  const RowTiling W = wide_tiling(cache->head_dim, group);
+  const RowTiling W = wide_tiling(cache->dtype, cache->head_dim, group);
   for (const auto& grp : P.groups) {
     DecodeLaunch D;
     std::memset(&D, 0, sizeof D);
@@ -656,7 +657,7 @@ int paged_attn_prefill(const pa_kv_cache* cache, const pa_stream* streams, int32
   if (!q || !out) return PA_EINVAL;
   const float ks = cache->dtype == PA_KV_FP8_E4M3 ? cache->k_scale : 1.f;
   const int32_t group = n_q_heads / cache->n_kv_heads;
-  const RowTiling T = prefill_tiling(cache->head_dim, group);
+  const RowTiling T = prefill_tiling(cache->dtype, cache->head_dim, group);
   for (size_t at = 0; at < live.size(); at += kMaxLaunchStreams) {
     pa::PrefillArgs A;
     std::memset(&A, 0, sizeof A);

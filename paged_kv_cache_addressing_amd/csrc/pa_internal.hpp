@@ -13,10 +13,11 @@ namespace pa {
 int launch_decode_partials(const DecodeArgs& A, int kv_dtype, int head_dim, int n_kv_heads,
                            hipStream_t st);
 int launch_decode_merge(const DecodeArgs& A, int head_dim, hipStream_t st);
-// MFMA columns ((row, q head) pairs) one prefill wave covers at head_dim.
-int prefill_columns(int head_dim);
-// MFMA columns one row-tile workgroup covers (all its waves) at head_dim.
-int prefill_wg_columns(int head_dim);
+// MFMA columns ((row, q head) pairs) one column group of the row-tile
+// kernel covers (a wave, or a producer/consumer wave pair).
+int prefill_columns(int kv_dtype, int head_dim);
+// MFMA columns one row-tile workgroup covers (all its column groups).
+int prefill_wg_columns(int kv_dtype, int head_dim);
 int launch_prefill(const PrefillArgs& A, int kv_dtype, int head_dim, hipStream_t st);
 int launch_write_kv(const WriteArgs& A, int kv_dtype, int head_dim, hipStream_t st);
 int launch_page_copy(const PageCopyArgs& A, hipStream_t st);

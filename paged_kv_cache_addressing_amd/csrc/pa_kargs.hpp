@@ -15,8 +15,24 @@ constexpr int kMaxLaunchStreams = 32; // streams per kernel launch; calls are ch
 // each wave fits in 256 registers and the SIMD interleaves two waves;
 // head_dim 128: 4 waves of 48 columns.  Both give a workgroup 128 or 192
 // columns sharing one set of K/V tiles.
+// Row-tile kernel shape.  A column group is the 16 * ntiles MFMA columns
+// that one wave holds, or, for bf16 at head_dim 256, one producer/consumer
+// wave pair (the producer runs S and the softmax, the consumer P.V).
+constexpr bool prefill_paired(int kv, int head_dim) { return kv == 0 && head_dim >= 256; }
 constexpr int prefill_waves(int head_dim) { return head_dim >= 256 ? 8 : 4; }
-constexpr int prefill_ntiles(int head_dim) { return head_dim >= 256 ? 1 : 3; }
+constexpr int prefill_ntiles(int kv, int head_dim) {
+  return prefill_paired(kv, head_dim) ? 2 : head_dim >= 256 ? 1 : 3;
+}
+constexpr int prefill_groups(int kv, int head_dim) {
+  return prefill_paired(kv, head_dim) ? prefill_waves(head_dim) / 2 : prefill_waves(head_dim);
+}
+// A workgroup's column count is the same for both KV dtypes, so a decode
+// plan (workspace and block counts) need not know the dtype.
+static_assert(prefill_groups(0, 256) * prefill_ntiles(0, 256) ==
+                  prefill_groups(1, 256) * prefill_ntiles(1, 256) &&
+              prefill_groups(0, 128) * prefill_ntiles(0, 128) ==
+                  prefill_groups(1, 128) * prefill_ntiles(1, 128),
+              "workgroup columns independent of the KV dtype");
 
 struct StreamArg {
   int32_t layout;       // 0 paged, 1 slab

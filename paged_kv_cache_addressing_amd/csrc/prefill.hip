@@ -9,10 +9,11 @@
 // output?").
 //
 // Work split.  A workgroup owns one kv head, HW of its q heads and a tile of
-// query rows; its NW waves own 16*NT MFMA columns each, a column being one
-// (row, q head) pair (column c of the workgroup is (c / HW, c % HW)).  At
-// head_dim 256: 8 waves of one n-tile (two waves per SIMD); at 128: 4 waves
-// of three.  The K/V tiles in LDS serve all HW heads, and the other head
+// query rows; its column groups own 16*NT MFMA columns each, a column being
+// one (row, q head) pair (column c of the workgroup is (c / HW, c % HW)).
+// bf16 at head_dim 256: 4 groups of two n-tiles, each a producer/consumer
+// wave pair on one SIMD; fp8 at 256: 8 waves of one n-tile (two per SIMD);
+// at 128: 4 waves of three.  The K/V tiles in LDS serve all HW heads, and the other head
 // groups of the same kv head run on the same XCD, so K/V also hit in L2.
 //   S^T (32 keys x 16NT cols) = K Q^T    : 2 m-tiles x NT n-tiles x D/32 k-steps
 //   O^T (D x 16NT cols)      += V^T P^T  : D/16 m-tiles x NT n-tiles x 1 k-step
@@ -96,7 +97,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   constexpr int MT = 2;                 // S^T m-tiles per step
   constexpr int KS = D / 32;            // QK k-steps
   constexpr int MD = D / 16;            // O^T m-tiles
-  constexpr int NT = prefill_ntiles(D);  // 16-column n-tiles per wave
+  constexpr bool PAIR = prefill_paired(KV, D);  // producer/consumer wave pairs
+  constexpr int NT = prefill_ntiles(KV, D);  // 16-column n-tiles per column group
+  constexpr int NG = prefill_groups(KV, D);  // column groups per workgroup
   constexpr int NW = prefill_waves(D);   // waves per workgroup
   constexpr int NTH = 64 * NW;          // threads per workgroup
   constexpr int KF = MT * KS;           // K fragments (1 KiB) per step
@@ -116,7 +119,12 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   constexpr int V8PW = VST / NTH;
   static_assert(kPage % BK == 0, "a step never straddles two pages");
 
-  __shared__ v4u lds[NSLOT * KSLOT + NVSLOT * VSLOT + (KV ? NSTG * (KST + VST) : 0)];
+  // Paired waves hand P (bf16, fragment order) and the rescale factors from
+  // producer to consumer through a two-slot ring per column group.
+  constexpr int PSLOT = NG * NT * 64;   // 16-byte entries per P slot
+  constexpr int ASLOT = NG * NT * 16;   // floats per rescale-factor slot
+  __shared__ v4u lds[NSLOT * KSLOT + NVSLOT * VSLOT + (KV ? NSTG * (KST + VST) : 0) +
+                     (PAIR ? 2 * PSLOT + 2 * ASLOT / 4 : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -154,7 +162,11 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   const int k_end = split_mode ? min(k_lo + A.split_keys, n_keys_t) : n_keys_t;
   const int v_lo = k_lo / BK;
   const int v_hi = k_end > k_lo ? (k_end + BK - 1) / BK : v_lo;
-  const bool wave_active = wave * 16 * NT < rows_here * HW;
+  // Column group of this wave; with pairs, waves g and g + NG share group g
+  // (and a SIMD): g is the producer, g + NG the consumer.
+  const int cg = PAIR ? wave % NG : wave;
+  const bool producer = !PAIR || wave < NG;
+  const bool wave_active = cg * 16 * NT < rows_here * HW;
   // first key some row of the tile may not see: past the first row's own
   // position, or (ancestor table) the stream's first row key
   const int mask_from = S.tree_mask ? S.first_pos : pos_first + 1;
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   v8bf qb[NT][KS];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int c = 16 * NT * wave + 16 * nt + n;
+    const int c = 16 * NT * cg + 16 * nt + n;
     const int rl = c / HW;
     chead[nt] = h0 + (c - rl * HW);
     crow[nt] = row0 + rl;
@@ -179,7 +191,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = KV ? 64 * (ks >> 1) + 16 * a + 8 * (ks & 1) : 32 * ks + 8 * a;
-      v4u x = load16(qp + d0 * 2);
+      v4u x = producer ? load16(qp + d0 * 2) : v4u{0, 0, 0, 0};
       if (!cok[nt]) x = v4u{0, 0, 0, 0};
       qb[nt][ks] = as_bf(x);
     }
@@ -472,153 +484,147 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   // positions, (v - v_lo) % 3, passed in as `ph` (a compile-time constant in
   // the unrolled steady state); V slots rotate through four.
   //
-  // Staggered waves.  With two waves per SIMD, the second wave of each SIMD
-  // (`lag`) takes the hand-off between its S product and its P.V product,
-  // the first after its P.V product.  Between two barriers one wave of a
-  // SIMD then runs S(v+1) and the softmax (VALU work, K reads) while the
-  // other runs P.V (V reads), so neither the matrix cores nor the LDS idle
-  // in one phase and saturate in the other.  A lagging wave reads V(v-1)
-  // after barrier v-1, which is why V needs a fourth slot: V(v+2), DMAed
-  // after that barrier, may not reuse V(v-1)'s slot.  Every wave still
-  // passes one barrier per step, in the same order.
+  // Paired waves (bf16, head_dim 256).  Each column group of 32 columns has
+  // a producer wave (S = K Q^T and the softmax; it holds Q, S and the running
+  // max and sum) and a consumer wave on the same SIMD (O += V P^T; it holds
+  // O).  In step v the producer computes P(v) and hands it over through LDS;
+  // the consumer applies it in step v+1.  Each K and V fragment read from
+  // LDS then feeds two MFMAs (32 columns) instead of one, which halves the
+  // fragment reads per product, and the two register sets (Q and S, or O)
+  // fit two waves per SIMD.
+  //
+  // Staggered waves (fp8, head_dim 256: eight waves of 16 columns each).
+  // The second wave of each SIMD (`lag`) takes the hand-off between its S
+  // product and its P.V product, the first after its P.V product, so one
+  // wave's S/softmax phase overlaps the other's P.V phase.
+  //
+  // Either way a wave may read V(v-1) after barrier v-1, which is why V
+  // needs a fourth slot: V(v+2), DMAed after that barrier, may not reuse
+  // V(v-1)'s slot.  Every wave passes one barrier per step, in the same order.
   static_assert(NSLOT == 3 && NSTG == 3 && NVSLOT == 4, "ring periods");
-  const bool lag = NW == 8 && wave >= NW / 2;
-  auto step = [&](int v, v4f (&Sc)[MT][NT], v4f (&Sn)[MT][NT], auto fast, auto ph) {
+  const bool lag = !PAIR && NW == 8 && wave >= NW / 2;
+  // DMAs of step v; returns how many bf16 tiles were issued (0, 1 = V, 2).
+  auto issue = [&](int v, auto fast, auto ph) -> int {
     constexpr bool FAST = decltype(fast)::value;
-    const int r0 = ph % 3, r1 = (ph + 1) % 3, r2 = (ph + 2) % 3;  // v, v+1 (and v+4), v+2
-    const int q0 = (v - v_lo) & 3, q1 = (v + 1 - v_lo) & 3, q2 = (v + 2 - v_lo) & 3;
+    const int r0 = ph % 3, r1 = (ph + 1) % 3;
     int issued = 0;
     if (KV == 0) {
-      if (FAST || v + 2 < v_hi) { dma_v(v + 2, q2); issued = 1; }
+      if (FAST || v + 2 < v_hi) { dma_v(v + 2, (v + 2 - v_lo) & 3); issued = 1; }
       if (FAST || v + 3 < v_hi) { dma_k(v + 3, r0); issued = 2; }
     } else {
       if (FAST || v + 4 < v_hi) dma8_k(v + 4, r1);
       if (FAST || v + 3 < v_hi) dma8_v(v + 3, r0);
     }
-    auto hand_off = [&]() {
-      if (KV == 0) {
-        if (FAST || issued == 2) wait_vmem<KPW + VPW>();
-        else if (issued == 1) wait_vmem<VPW>();
-        else wait_vmem<0>();
-      } else {
-        // K(v+2) and V(v+1) have landed once at most the DMAs issued in steps
-        // v-1 and v (K(v+3), V(v+2), K(v+4), V(v+3), those that exist) remain.
-        const int r = v_hi - 1 - v;
-        if (FAST || r >= 4) wait_vmem<2 * (K8PW + V8PW)>();
-        else if (r == 3) wait_vmem<K8PW + 2 * V8PW>();
-        else if (r == 2) wait_vmem<V8PW>();
-        else wait_vmem<0>();
-        if (FAST) convert_fp8(v + 2, r2, v + 1, r1, q1, std::false_type{});
-        else convert_fp8(v + 2 < v_hi ? v + 2 : -1, r2, v + 1 < v_hi ? v + 1 : -1, r1, q1,
-                         std::true_type{});
-      }
-      lds_barrier();
-      if (!FAST && KV == 0 && v + 1 < v_hi && (v + 1) * BK + BK > n_keys_t) {
-        zero_tail_bf16(v + 1, q1);
-        lds_barrier();
-      }
-    };
-    v8bf P[NT];
-    float alpha[NT];
-    if (wave_active) {
-      if (!FAST && v * BK + BK - 1 >= mask_from) mask(v, Sc);
-      // K(v+1), or stale data past the end (unused).  This phase (matrix
-      // products, softmax and K reads) is the longer one, so its wave takes
-      // issue priority over a P.V-phase wave on the same SIMD.
-      __builtin_amdgcn_s_setprio(1);
-      qk_softmax(r1 * KSLOT, Sn, Sc, P, alpha);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    if (lag) hand_off();
-    if (wave_active) {
-      bool moved = false;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) moved |= alpha[nt] != 1.f;
-      if (__any(moved)) {
-#pragma unroll
-        for (int md = 0; md < MD; ++md)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) o[md][nt] *= alpha[nt];
-      }
-      pv(q0 * VSLOT, P);
-    }
-    if (!lag) hand_off();
+    return issued;
   };
-
-  // Prologue: K(v_lo), V(v_lo), K(v_lo+1) resident as bf16 (bf16 also has
-  // K(v_lo+2), V(v_lo+1) in flight; fp8 has the codes of V(v_lo+1..v_lo+2)
-  // and K(v_lo+2..v_lo+3) in flight); S(v_lo) computed; then the slot of
-  // K(v_lo) may be reused.  A work item with no keys skips to its output.
-  if (v_hi > v_lo) {
-    const int n_st = v_hi - v_lo;
-    v4f S0[MT][NT], S1[MT][NT];
+  auto hand_off = [&](int v, auto fast, auto ph, int issued) {
+    constexpr bool FAST = decltype(fast)::value;
+    const int r1 = (ph + 1) % 3, r2 = (ph + 2) % 3;
+    const int q1 = (v + 1 - v_lo) & 3;
     if (KV == 0) {
-      dma_k(v_lo, 0);
-      dma_v(v_lo, 0);
-      if (n_st > 1) dma_k(v_lo + 1, 1);
-      if (n_st > 1) dma_v(v_lo + 1, 1);
-      if (n_st > 2) dma_k(v_lo + 2, 2);
-      if (n_st > 2) wait_vmem<KPW + VPW>();
-      else if (n_st > 1) wait_vmem<VPW>();
+      if (FAST || issued == 2) wait_vmem<KPW + VPW>();
+      else if (issued == 1) wait_vmem<VPW>();
       else wait_vmem<0>();
     } else {
-      dma8_k(v_lo, 0);
-      dma8_v(v_lo, 0);
-      if (n_st > 1) dma8_k(v_lo + 1, 1);
-      wait_vmem<0>();
-      convert_fp8(v_lo, 0, v_lo, 0, 0, std::true_type{});
-      if (n_st > 1) convert_fp8(v_lo + 1, 1, -1, 0, 0, std::true_type{});
-      // the staging reads above finish before K(v_lo+3) reuses K(v_lo)'s entries
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (n_st > 1) dma8_v(v_lo + 1, 1);
-      if (n_st > 2) dma8_k(v_lo + 2, 2);
-      if (n_st > 2) dma8_v(v_lo + 2, 2);
-      if (n_st > 3) dma8_k(v_lo + 3, 0);
+      // K(v+2) and V(v+1) have landed once at most the DMAs issued in steps
+      // v-1 and v (K(v+3), V(v+2), K(v+4), V(v+3), those that exist) remain.
+      const int r = v_hi - 1 - v;
+      if (FAST || r >= 4) wait_vmem<2 * (K8PW + V8PW)>();
+      else if (r == 3) wait_vmem<K8PW + 2 * V8PW>();
+      else if (r == 2) wait_vmem<V8PW>();
+      else wait_vmem<0>();
+      if (FAST) convert_fp8(v + 2, r2, v + 1, r1, q1, std::false_type{});
+      else convert_fp8(v + 2 < v_hi ? v + 2 : -1, r2, v + 1 < v_hi ? v + 1 : -1, r1, q1,
+                       std::true_type{});
     }
-    __syncthreads();
-    if (KV == 0 && v_lo * BK + BK > n_keys_t) {
-      zero_tail_bf16(v_lo, 0);
-      __syncthreads();
+    lds_barrier();
+    if (!FAST && KV == 0 && v + 1 < v_hi && (v + 1) * BK + BK > n_keys_t) {
+      zero_tail_bf16(v + 1, q1);
+      lds_barrier();
     }
-    if (wave_active) qk(0, S0);
-    __syncthreads();
+  };
+  // O *= alpha where some column's running max moved (rarely).
+  auto rescale = [&](const float (&alpha)[NT]) {
+    bool moved = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) moved |= alpha[nt] != 1.f;
+    if (__any(moved)) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[md][nt] *= alpha[nt];
+    }
+  };
+  // S(v+1) and softmax(v), raising the wave's issue priority: this phase
+  // (matrix products, softmax and K reads) is the longer one, so it goes
+  // ahead of a P.V-only wave on the same SIMD.
+  auto s_phase = [&](int v, v4f (&Sc)[MT][NT], v4f (&Sn)[MT][NT], auto fast, auto ph,
+                     v8bf (&P)[NT], float (&alpha)[NT]) {
+    constexpr bool FAST = decltype(fast)::value;
+    if (!FAST && v * BK + BK - 1 >= mask_from) mask(v, Sc);
+    __builtin_amdgcn_s_setprio(1);
+    // K(v+1), or stale data past the end (unused)
+    qk_softmax(((ph + 1) % 3) * KSLOT, Sn, Sc, P, alpha);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // A wave that runs both phases of its columns.
+  auto step = [&](int v, v4f (&Sc)[MT][NT], v4f (&Sn)[MT][NT], auto fast, auto ph) {
+    const int issued = issue(v, fast, ph);
+    v8bf P[NT];
+    float alpha[NT];
+    if (wave_active) s_phase(v, Sc, Sn, fast, ph, P, alpha);
+    if (lag) hand_off(v, fast, ph, issued);
+    if (wave_active) {
+      rescale(alpha);
+      pv(((v - v_lo) & 3) * VSLOT, P);
+    }
+    if (!lag) hand_off(v, fast, ph, issued);
+  };
+  // Paired waves: the P ring (slot (v - v_lo) & 1; 16 bytes per lane per
+  // n-tile) and the rescale factors (one per column).
+  v4u* const Pbase = lds + NSLOT * KSLOT + NVSLOT * VSLOT + (KV ? NSTG * (KST + VST) : 0);
+  float* const Abase = reinterpret_cast<float*>(Pbase + 2 * PSLOT);
+  auto pstep = [&](int v, v4f (&Sc)[MT][NT], v4f (&Sn)[MT][NT], auto fast, auto ph) {
+    const int issued = issue(v, fast, ph);
+    if (wave_active) {
+      v8bf P[NT];
+      float alpha[NT];
+      s_phase(v, Sc, Sn, fast, ph, P, alpha);
+      const int sl = (v - v_lo) & 1;
+      v4u* pd = Pbase + sl * PSLOT + cg * NT * 64 + lane;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) pd[nt * 64] = __builtin_bit_cast(v4u, P[nt]);
+      if (a == 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) Abase[sl * ASLOT + (cg * NT + nt) * 16 + n] = alpha[nt];
+      }
+    }
+    hand_off(v, fast, ph, issued);
+  };
+  // O += V(u) P(u)^T with P(u) from the ring (published by barrier u).
+  auto consume = [&](int u) {
+    const int sl = (u - v_lo) & 1;
+    const v4u* ps = Pbase + sl * PSLOT + cg * NT * 64 + lane;
+    v8bf P[NT];
+    float alpha[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      P[nt] = as_bf(ps[nt * 64]);
+      alpha[nt] = Abase[sl * ASLOT + (cg * NT + nt) * 16 + n];
+    }
+    rescale(alpha);
+    pv(((u - v_lo) & 3) * VSLOT, P);
+  };
+  auto cstep = [&](int v, auto fast, auto ph) {
+    const int issued = issue(v, fast, ph);
+    if (wave_active && v > v_lo) consume(v - 1);
+    hand_off(v, fast, ph, issued);
+  };
 
-    // Steps [v_lo, v_fast) are steady state: v+3 (bf16) or v+4 (fp8) is
-    // still in range, no key of the step is maskable (before mask_from),
-    // and the next V step holds no key at or past n_keys_t.
-    const int v_fast = max(v_lo, min(min(v_hi - (KV ? 4 : 3), mask_from / BK),
-                                     n_keys_t / BK - 1));
-    // The steady state runs three steps per iteration, one per ring
-    // position, so every slot address is a constant; S(v+1) alternates
-    // between S0 and S1.
-    auto copy_s = [&](v4f (&dst)[MT][NT], v4f (&src)[MT][NT]) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) dst[mt][nt] = src[mt][nt];
-    };
-    typedef std::integral_constant<int, 0> P0;
-    typedef std::integral_constant<int, 1> P1;
-    typedef std::integral_constant<int, 2> P2;
-    int v = v_lo;
-    for (; v + 3 <= v_fast; v += 3) {
-      step(v, S0, S1, std::true_type{}, P0{});
-      step(v + 1, S1, S0, std::true_type{}, P1{});
-      step(v + 2, S0, S1, std::true_type{}, P2{});
-      copy_s(S0, S1);
-    }
-    for (; v < v_hi; ++v) {
-      step(v, S0, S1, std::false_type{}, (v - v_lo) % 3);
-      copy_s(S0, S1);
-    }
-  }
-
-  if (!wave_active) return;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float l = l_run[nt];
-    l = rows4_sum(l);
-    if (!cok[nt]) continue;
+  // Output of column n-tile nt with row sum l and running max m*c (log2
+  // units).
+  auto write_out = [&](int nt, float l, float mc) {
+    if (!cok[nt]) return;
     if (split_mode) {
       // Partial of (row, head, split): p was exp2(s*c - m_run*c), so the
       // split's m in log2 units is exactly m_run*c; o stays in stored-V units.
@@ -627,14 +633,14 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       // A rejected page id poisons m as a NaN bit pattern (this file is built
       // without NaN semantics, so no floating-point NaN is ever formed here).
       if (a == 0) {
-        const uint32_t mb = bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, m_run[nt] * c);
+        const uint32_t mb = bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, mc);
         reinterpret_cast<uint32_t*>(A.ws_ml)[2 * slot] = mb;
         A.ws_ml[2 * slot + 1] = l;
       }
       float* dst = A.ws_o + slot * D + 4 * a;
 #pragma unroll
       for (int md = 0; md < MD; ++md) *reinterpret_cast<v4f*>(dst + 16 * md) = o[md][nt];
-      continue;
+      return;
     }
     const float f = A.v_scale / l;
     uint16_t* dst =
@@ -648,6 +654,138 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       if (bad) w = v2u{0x7FC07FC0u, 0x7FC07FC0u};  // bf16 NaN bits for a rejected page id
       *reinterpret_cast<v2u*>(dst + 16 * md) = w;
     }
+  };
+
+  // The rest of the work item for one role: 0 = producer of a pair,
+  // 1 = consumer of a pair, 2 = a wave that runs both phases.  Each role is
+  // its own inlined copy with no path joining another role's, so the
+  // registers a role does not touch (Q and S for a consumer, O for a
+  // producer) are free in its copy.
+  auto run = [&](auto role) {
+    constexpr int R = decltype(role)::value;
+    // Prologue: K(v_lo), V(v_lo), K(v_lo+1) resident as bf16 (bf16 also has
+    // K(v_lo+2), V(v_lo+1) in flight; fp8 has the codes of V(v_lo+1..v_lo+2)
+    // and K(v_lo+2..v_lo+3) in flight); S(v_lo) computed; then the slot of
+    // K(v_lo) may be reused.  A work item with no keys skips to its output.
+    if (v_hi > v_lo) {
+      const int n_st = v_hi - v_lo;
+      v4f S0[MT][NT], S1[MT][NT];
+      if (KV == 0) {
+        dma_k(v_lo, 0);
+        dma_v(v_lo, 0);
+        if (n_st > 1) dma_k(v_lo + 1, 1);
+        if (n_st > 1) dma_v(v_lo + 1, 1);
+        if (n_st > 2) dma_k(v_lo + 2, 2);
+        if (n_st > 2) wait_vmem<KPW + VPW>();
+        else if (n_st > 1) wait_vmem<VPW>();
+        else wait_vmem<0>();
+      } else {
+        dma8_k(v_lo, 0);
+        dma8_v(v_lo, 0);
+        if (n_st > 1) dma8_k(v_lo + 1, 1);
+        wait_vmem<0>();
+        convert_fp8(v_lo, 0, v_lo, 0, 0, std::true_type{});
+        if (n_st > 1) convert_fp8(v_lo + 1, 1, -1, 0, 0, std::true_type{});
+        // the staging reads above finish before K(v_lo+3) reuses K(v_lo)'s entries
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (n_st > 1) dma8_v(v_lo + 1, 1);
+        if (n_st > 2) dma8_k(v_lo + 2, 2);
+        if (n_st > 2) dma8_v(v_lo + 2, 2);
+        if (n_st > 3) dma8_k(v_lo + 3, 0);
+      }
+      __syncthreads();
+      if (KV == 0 && v_lo * BK + BK > n_keys_t) {
+        zero_tail_bf16(v_lo, 0);
+        __syncthreads();
+      }
+      if (R != 1 && wave_active) qk(0, S0);
+      __syncthreads();
+
+      // Steps [v_lo, v_fast) are steady state: v+3 (bf16) or v+4 (fp8) is
+      // still in range, no key of the step is maskable (before mask_from),
+      // and the next V step holds no key at or past n_keys_t.
+      const int v_fast = max(v_lo, min(min(v_hi - (KV ? 4 : 3), mask_from / BK),
+                                       n_keys_t / BK - 1));
+      // The steady state runs three steps per iteration, one per ring
+      // position, so every slot address is a constant; S(v+1) alternates
+      // between S0 and S1.
+      auto copy_s = [&](v4f (&dst)[MT][NT], v4f (&src)[MT][NT]) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) dst[mt][nt] = src[mt][nt];
+      };
+      typedef std::integral_constant<int, 0> P0;
+      typedef std::integral_constant<int, 1> P1;
+      typedef std::integral_constant<int, 2> P2;
+      int v = v_lo;
+      if constexpr (R == 0) {
+        for (; v + 3 <= v_fast; v += 3) {
+          pstep(v, S0, S1, std::true_type{}, P0{});
+          pstep(v + 1, S1, S0, std::true_type{}, P1{});
+          pstep(v + 2, S0, S1, std::true_type{}, P2{});
+          copy_s(S0, S1);
+        }
+        for (; v < v_hi; ++v) {
+          pstep(v, S0, S1, std::false_type{}, (v - v_lo) % 3);
+          copy_s(S0, S1);
+        }
+      } else if constexpr (R == 1) {
+        for (; v + 3 <= v_fast; v += 3) {
+          cstep(v, std::true_type{}, P0{});
+          cstep(v + 1, std::true_type{}, P1{});
+          cstep(v + 2, std::true_type{}, P2{});
+        }
+        for (; v < v_hi; ++v) cstep(v, std::false_type{}, (v - v_lo) % 3);
+        // P(v_hi - 1), published by the last step's barrier
+        if (wave_active) consume(v_hi - 1);
+      } else {
+        for (; v + 3 <= v_fast; v += 3) {
+          step(v, S0, S1, std::true_type{}, P0{});
+          step(v + 1, S1, S0, std::true_type{}, P1{});
+          step(v + 2, S0, S1, std::true_type{}, P2{});
+          copy_s(S0, S1);
+        }
+        for (; v < v_hi; ++v) {
+          step(v, S0, S1, std::false_type{}, (v - v_lo) % 3);
+          copy_s(S0, S1);
+        }
+      }
+    }
+
+    if constexpr (R == 0) {
+      // The producer hands its row sums and running maxima to the consumer
+      // through LDS (the K slots, free once the last step's barrier passed).
+      float* X = reinterpret_cast<float*>(lds);
+      if (wave_active) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float l = rows4_sum(l_run[nt]);
+          if (a == 0) {
+            X[(cg * NT + nt) * 32 + n] = l;
+            X[(cg * NT + nt) * 32 + 16 + n] = m_run[nt] * c;
+          }
+        }
+      }
+      __syncthreads();
+    } else if constexpr (R == 1) {
+      const float* X = reinterpret_cast<const float*>(lds);
+      __syncthreads();
+      if (!wave_active) return;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        write_out(nt, X[(cg * NT + nt) * 32 + n], X[(cg * NT + nt) * 32 + 16 + n]);
+    } else {
+      if (!wave_active) return;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) write_out(nt, rows4_sum(l_run[nt]), m_run[nt] * c);
+    }
+  };
+  if constexpr (PAIR) {
+    if (producer) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, 2>{});
   }
 }
 
@@ -658,8 +796,10 @@ static int launch_prefill_t(const PrefillArgs& A, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-int prefill_columns(int head_dim) { return 16 * prefill_ntiles(head_dim); }
-int prefill_wg_columns(int head_dim) { return prefill_waves(head_dim) * prefill_columns(head_dim); }
+int prefill_columns(int kv_dtype, int head_dim) { return 16 * prefill_ntiles(kv_dtype, head_dim); }
+int prefill_wg_columns(int kv_dtype, int head_dim) {
+  return prefill_groups(kv_dtype, head_dim) * prefill_columns(kv_dtype, head_dim);
+}
 
 int launch_prefill(const PrefillArgs& A, int kv_dtype, int head_dim, hipStream_t st) {
   if (kv_dtype == 0 && head_dim == 128) return launch_prefill_t<0, 128>(A, st);
