@@ -105,6 +105,8 @@ DECODE_CASES = [
      ["paged", "slab", "paged"], 4096),
     ("verify-g16-d128-two-tiles", 32, 2, 128, "bf16", [5000], [16], None, 2048),
     ("verify-g8-d256-fp8", 32, 4, 256, "fp8", [9000, 4096], [16, 9], None, 4096),
+    # bf16 at head_dim 256 runs producer/consumer wave pairs: 8 heads per tile
+    ("verify-g8-d256-bf16", 32, 4, 256, "bf16", [9000, 4096], [16, 9], None, 4096),
 ]
 
 
@@ -244,6 +246,9 @@ PREFILL_CASES = [
     ("fp8", 6, 2, 256, "fp8", [1000], [300], None),
     ("two-streams-mixed", 6, 2, 256, "bf16", [700, 1200], [129, 300], ["paged", "slab"]),
     ("fp8-d128-mixed", 4, 1, 128, "fp8", [513, 2000], [200, 77], ["slab", "paged"]),
+    # other group sizes on the paired bf16 kernel: 8 heads (16-row tiles) and 1
+    ("g8-rows200", 16, 2, 256, "bf16", [1500], [200], None),
+    ("g1-mha", 2, 2, 256, "bf16", [600], [130], None),
 ]
 
 
