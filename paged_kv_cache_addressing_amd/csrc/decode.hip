@@ -101,23 +101,24 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   // The wave's chunks, in order: its pages p_lo + wave, + NW, ..., each cut
   // into CK-key chunks up to the split's end.  Two register sets alternate:
   // the next chunk's K and V loads are issued before this chunk's products,
-  // so a wave always has a chunk of bytes in flight while it computes.
+  // so a wave always has a chunk of bytes in flight while it computes.  Each
+  // K/V byte is read once, so the loads are streaming (nontemporal).
   auto load = [&](v4u (&kr)[KL], v4u (&vr)[MD], const PageTile& T, int c0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint8_t* kp = T.k + (int64_t)(c0 + krow + 4 * mt) * D * ESZ;
       if (KV) {
 #pragma unroll
-        for (int kq = 0; kq < KS / 2; ++kq) kr[mt * (KS / 2) + kq] = load16(kp + 64 * kq + 16 * a);
+        for (int kq = 0; kq < KS / 2; ++kq) kr[mt * (KS / 2) + kq] = load16_stream(kp + 64 * kq + 16 * a);
       } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[mt * KS + ks] = load16(kp + (32 * ks + 8 * a) * 2);
+        for (int ks = 0; ks < KS; ++ks) kr[mt * KS + ks] = load16_stream(kp + (32 * ks + 8 * a) * 2);
       }
     }
     // V block of this chunk (CK == 64/ESZ keys): D rows of 64 bytes.
     const uint8_t* vb = T.v + (int64_t)c0 * D * ESZ + (8 * KK * a) * ESZ;
 #pragma unroll
-    for (int md = 0; md < MD; ++md) vr[md] = load16(vb + (16 * md + n) * 64);
+    for (int md = 0; md < MD; ++md) vr[md] = load16_stream(vb + (16 * md + n) * 64);
   };
   auto chunk = [&](v4u (&kr)[KL], v4u (&vr)[MD], int p, int c0) {
     v4f sacc[MT];
