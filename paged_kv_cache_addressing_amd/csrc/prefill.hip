@@ -13,8 +13,9 @@
 // one (row, q head) pair (column c of the workgroup is (c / HW, c % HW)).
 // bf16 at head_dim 256: 4 groups of two n-tiles, each a producer/consumer
 // wave pair on one SIMD; fp8 at 256: 8 waves of one n-tile (two per SIMD);
-// at 128: 4 waves of three.  The K/V tiles in LDS serve all HW heads, and the other head
-// groups of the same kv head run on the same XCD, so K/V also hit in L2.
+// at 128: 4 waves of three.  The K/V tiles in LDS serve all HW heads, and
+// the other head groups of the same kv head run on the same XCD, so K/V
+// also hit in L2.
 //   S^T (32 keys x 16NT cols) = K Q^T    : 2 m-tiles x NT n-tiles x D/32 k-steps
 //   O^T (D x 16NT cols)      += V^T P^T  : D/16 m-tiles x NT n-tiles x 1 k-step
 // The key order inside a step is permuted so each lane's S^T C-rows are the
@@ -34,9 +35,10 @@
 // lane l's 16 bytes at l*16, so ds_read_b128 is conflict-free).  bf16 arrives
 // by buffer_load_dwordx4 ... lds straight into LDS, two steps ahead; fp8 codes
 // arrive the same way into a staging ring three steps ahead and are
-// converted to bf16 fragment order once, one step ahead.  In step v
-// a wave computes S(v+1) = K(v+1) Q^T on the matrix cores while the VALU does
-// the softmax of S(v), then accumulates O += V(v) P(v).
+// converted to bf16 fragment order once, one step ahead.  In step v the
+// S product S(v+1) = K(v+1) Q^T runs on the matrix cores while the VALU does
+// the softmax of S(v); O += V(v) P(v) follows in the same wave, or (wave
+// pairs) in the consumer wave one step later.
 //
 // Softmax.  Logits stay raw until exp2(fma(s, c, -m c)).  A row's running max
 // moves only when the new maximum exceeds it by more than 2^8 in probability
