@@ -16,9 +16,9 @@ constexpr int kMaxLaunchStreams = 32; // streams per kernel launch; calls are ch
 // head_dim 128: 4 waves of 48 columns.  Both give a workgroup 128 or 192
 // columns sharing one set of K/V tiles.
 // Row-tile kernel shape.  A column group is the 16 * ntiles MFMA columns
-// that one wave holds, or, for bf16 at head_dim 256, one producer/consumer
-// wave pair (the producer runs S and the softmax, the consumer P.V).
-constexpr bool prefill_paired(int kv, int head_dim) { return kv == 0 && head_dim >= 256; }
+// that one wave holds, or, at head_dim 256, one producer/consumer wave pair
+// (the producer runs S and the softmax, the consumer P.V).
+constexpr bool prefill_paired(int kv, int head_dim) { return (kv == 0 || kv == 1) && head_dim >= 256; }
 constexpr int prefill_waves(int head_dim) { return head_dim >= 256 ? 8 : 4; }
 constexpr int prefill_ntiles(int kv, int head_dim) {
   return prefill_paired(kv, head_dim) ? 2 : head_dim >= 256 ? 1 : 3;

@@ -108,8 +108,10 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   constexpr int VF = MD;                // V fragments per step
   constexpr int KPW = KF / NW;          // DMA fragments per wave per step
   constexpr int VPW = VF / NW;
-  constexpr int NSLOT = 3;              // K slots
-  constexpr int NVSLOT = 4;             // V slots (see the step schedule)
+  // K and V slot rings (see the step schedule): bf16 DMAs K three and V two
+  // steps ahead; fp8 converts K(v+2) and V(v+1) into their slots in step v.
+  constexpr int NSLOT = KV ? 2 : 3;     // K slots
+  constexpr int NVSLOT = KV ? 3 : 4;    // V slots
   constexpr int KSLOT = KF * 64;        // 16-byte entries per slot
   constexpr int VSLOT = VF * 64;
   // fp8: raw codes land in a staging ring (16-byte entries per step) and are
@@ -306,9 +308,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       dma16(rs, off, 0, dst + (q >> 6) * 64);
     }
   };
-  auto convert_fp8 = [&](int vk, int slk, int vv, int stv, int slv, auto may_tail) {
+  auto convert_fp8 = [&](int vk, int stk, int slk, int vv, int stv, int slv, auto may_tail) {
     if (vk >= 0) {
-      const v4u* St = Sbase + slk * (KST + VST);
+      const v4u* St = Sbase + stk * (KST + VST);
       v4u* Ls = Kbase + slk * KSLOT;
 #pragma unroll
       for (int i = 0; i < K8PW; ++i) {
@@ -481,12 +483,13 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   // and the hand-off: wait for the next steps' tiles, then a barrier that
   // publishes them and releases the slots read before it.
   // FAST is the steady state (every prefetch in range, no causal mask, no
-  // key-range tail), where the step runs without any of those checks.  K
-  // slots and fp8 staging entries rotate with the step through three ring
-  // positions, (v - v_lo) % 3, passed in as `ph` (a compile-time constant in
-  // the unrolled steady state); V slots rotate through four.
+  // key-range tail), where the step runs without any of those checks.  The
+  // fp8 staging entries (and bf16 K slots) rotate with the step through three
+  // ring positions, (v - v_lo) % 3, passed in as `ph` (a compile-time
+  // constant in the unrolled steady state); the other rings use their own
+  // period.
   //
-  // Paired waves (bf16, head_dim 256).  Each column group of 32 columns has
+  // Paired waves (head_dim 256).  Each column group of 32 columns has
   // a producer wave (S = K Q^T and the softmax; it holds Q, S and the running
   // max and sum) and a consumer wave on the same SIMD (O += V P^T; it holds
   // O).  In step v the producer computes P(v) and hands it over through LDS;
@@ -495,24 +498,22 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   // fragment reads per product, and the two register sets (Q and S, or O)
   // fit two waves per SIMD.
   //
-  // Staggered waves (fp8, head_dim 256: eight waves of 16 columns each).
-  // The second wave of each SIMD (`lag`) takes the hand-off between its S
-  // product and its P.V product, the first after its P.V product, so one
-  // wave's S/softmax phase overlaps the other's P.V phase.
-  //
-  // Either way a wave may read V(v-1) after barrier v-1, which is why V
-  // needs a fourth slot: V(v+2), DMAed after that barrier, may not reuse
-  // V(v-1)'s slot.  Every wave passes one barrier per step, in the same order.
-  static_assert(NSLOT == 3 && NSTG == 3 && NVSLOT == 4, "ring periods");
-  const bool lag = !PAIR && NW == 8 && wave >= NW / 2;
+  // The consumer reads V(v-1) after barrier v-1, in step v.  With bf16,
+  // V(v+2) is DMAed in step v, so V has four slots (V(v-1) .. V(v+2)); K has
+  // three (K(v+1) is read while K(v+2), K(v+3) land).  With fp8, step v
+  // converts V(v+1) and K(v+2) from staging, so V needs three slots and K
+  // two.  Every wave passes one barrier per step, in the same order.
+  static_assert(NSTG == 3 && NSLOT == (KV ? 2 : 3) && NVSLOT == (KV ? 3 : 4), "ring periods");
+  auto kslot = [&](int u) { return (u - v_lo) % NSLOT; };
+  auto vslot = [&](int u) { return (u - v_lo) % NVSLOT; };
   // DMAs of step v; returns how many bf16 tiles were issued (0, 1 = V, 2).
   auto issue = [&](int v, auto fast, auto ph) -> int {
     constexpr bool FAST = decltype(fast)::value;
-    const int r0 = ph % 3, r1 = (ph + 1) % 3;
+    const int r0 = ph % 3, r1 = (ph + 1) % 3;  // staging of v+3, v+4
     int issued = 0;
     if (KV == 0) {
-      if (FAST || v + 2 < v_hi) { dma_v(v + 2, (v + 2 - v_lo) & 3); issued = 1; }
-      if (FAST || v + 3 < v_hi) { dma_k(v + 3, r0); issued = 2; }
+      if (FAST || v + 2 < v_hi) { dma_v(v + 2, vslot(v + 2)); issued = 1; }
+      if (FAST || v + 3 < v_hi) { dma_k(v + 3, kslot(v + 3)); issued = 2; }
     } else {
       if (FAST || v + 4 < v_hi) dma8_k(v + 4, r1);
       if (FAST || v + 3 < v_hi) dma8_v(v + 3, r0);
@@ -521,8 +522,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   };
   auto hand_off = [&](int v, auto fast, auto ph, int issued) {
     constexpr bool FAST = decltype(fast)::value;
-    const int r1 = (ph + 1) % 3, r2 = (ph + 2) % 3;
-    const int q1 = (v + 1 - v_lo) & 3;
+    const int r1 = (ph + 1) % 3, r2 = (ph + 2) % 3;  // staging of v+1, v+2
     if (KV == 0) {
       if (FAST || issued == 2) wait_vmem<KPW + VPW>();
       else if (issued == 1) wait_vmem<VPW>();
@@ -535,13 +535,13 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       else if (r == 3) wait_vmem<K8PW + 2 * V8PW>();
       else if (r == 2) wait_vmem<V8PW>();
       else wait_vmem<0>();
-      if (FAST) convert_fp8(v + 2, r2, v + 1, r1, q1, std::false_type{});
-      else convert_fp8(v + 2 < v_hi ? v + 2 : -1, r2, v + 1 < v_hi ? v + 1 : -1, r1, q1,
-                       std::true_type{});
+      if (FAST) convert_fp8(v + 2, r2, kslot(v + 2), v + 1, r1, vslot(v + 1), std::false_type{});
+      else convert_fp8(v + 2 < v_hi ? v + 2 : -1, r2, kslot(v + 2), v + 1 < v_hi ? v + 1 : -1, r1,
+                       vslot(v + 1), std::true_type{});
     }
     lds_barrier();
     if (!FAST && KV == 0 && v + 1 < v_hi && (v + 1) * BK + BK > n_keys_t) {
-      zero_tail_bf16(v + 1, q1);
+      zero_tail_bf16(v + 1, vslot(v + 1));
       lds_barrier();
     }
   };
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
     if (!FAST && v * BK + BK - 1 >= mask_from) mask(v, Sc);
     __builtin_amdgcn_s_setprio(1);
     // K(v+1), or stale data past the end (unused)
-    qk_softmax(((ph + 1) % 3) * KSLOT, Sn, Sc, P, alpha);
+    qk_softmax(kslot(v + 1) * KSLOT, Sn, Sc, P, alpha);
     __builtin_amdgcn_s_setprio(0);
   };
   // A wave that runs both phases of its columns.
@@ -575,12 +575,11 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
     v8bf P[NT];
     float alpha[NT];
     if (wave_active) s_phase(v, Sc, Sn, fast, ph, P, alpha);
-    if (lag) hand_off(v, fast, ph, issued);
     if (wave_active) {
       rescale(alpha);
-      pv(((v - v_lo) & 3) * VSLOT, P);
+      pv(vslot(v) * VSLOT, P);
     }
-    if (!lag) hand_off(v, fast, ph, issued);
+    hand_off(v, fast, ph, issued);
   };
   // Paired waves: the P ring (slot (v - v_lo) & 1; 16 bytes per lane per
   // n-tile) and the rescale factors (one per column).
@@ -615,7 +614,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       alpha[nt] = Abase[sl * ASLOT + (cg * NT + nt) * 16 + n];
     }
     rescale(alpha);
-    pv(((u - v_lo) & 3) * VSLOT, P);
+    pv(vslot(u) * VSLOT, P);
   };
   auto cstep = [&](int v, auto fast, auto ph) {
     const int issued = issue(v, fast, ph);
@@ -686,8 +685,8 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
         dma8_v(v_lo, 0);
         if (n_st > 1) dma8_k(v_lo + 1, 1);
         wait_vmem<0>();
-        convert_fp8(v_lo, 0, v_lo, 0, 0, std::true_type{});
-        if (n_st > 1) convert_fp8(v_lo + 1, 1, -1, 0, 0, std::true_type{});
+        convert_fp8(v_lo, 0, 0, v_lo, 0, 0, std::true_type{});
+        if (n_st > 1) convert_fp8(v_lo + 1, 1, 1, -1, 0, 0, std::true_type{});
         // the staging reads above finish before K(v_lo+3) reuses K(v_lo)'s entries
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (n_st > 1) dma8_v(v_lo + 1, 1);
