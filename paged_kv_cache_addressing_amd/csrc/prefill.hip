@@ -517,19 +517,13 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
     } else {
       if (FAST || v + 4 < v_hi) dma8_k(v + 4, r1);
       if (FAST || v + 3 < v_hi) dma8_v(v + 3, r0);
-    }
-    return issued;
-  };
-  auto hand_off = [&](int v, auto fast, auto ph, int issued) {
-    constexpr bool FAST = decltype(fast)::value;
-    const int r1 = (ph + 1) % 3, r2 = (ph + 2) % 3;  // staging of v+1, v+2
-    if (KV == 0) {
-      if (FAST || issued == 2) wait_vmem<KPW + VPW>();
-      else if (issued == 1) wait_vmem<VPW>();
-      else wait_vmem<0>();
-    } else {
-      // K(v+2) and V(v+1) have landed once at most the DMAs issued in steps
-      // v-1 and v (K(v+3), V(v+2), K(v+4), V(v+3), those that exist) remain.
+      // Then convert K(v+2) and V(v+1) (staging positions r2 and r1) into
+      // their bf16 slots at the start of the step, so the conversion
+      // overlaps this step's products on the SIMD's other wave; barrier v
+      // publishes them.  Their codes have landed once at most the DMAs
+      // issued in steps v-1 and v (K(v+3), V(v+2), K(v+4), V(v+3), those
+      // that exist) remain.
+      const int r2 = (ph + 2) % 3;
       const int r = v_hi - 1 - v;
       if (FAST || r >= 4) wait_vmem<2 * (K8PW + V8PW)>();
       else if (r == 3) wait_vmem<K8PW + 2 * V8PW>();
@@ -538,6 +532,16 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       if (FAST) convert_fp8(v + 2, r2, kslot(v + 2), v + 1, r1, vslot(v + 1), std::false_type{});
       else convert_fp8(v + 2 < v_hi ? v + 2 : -1, r2, kslot(v + 2), v + 1 < v_hi ? v + 1 : -1, r1,
                        vslot(v + 1), std::true_type{});
+    }
+    return issued;
+  };
+  auto hand_off = [&](int v, auto fast, auto ph, int issued) {
+    constexpr bool FAST = decltype(fast)::value;
+    (void)ph;
+    if (KV == 0) {
+      if (FAST || issued == 2) wait_vmem<KPW + VPW>();
+      else if (issued == 1) wait_vmem<VPW>();
+      else wait_vmem<0>();
     }
     lds_barrier();
     if (!FAST && KV == 0 && v + 1 < v_hi && (v + 1) * BK + BK > n_keys_t) {
