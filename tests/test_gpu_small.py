@@ -107,6 +107,10 @@ DECODE_CASES = [
     ("verify-g8-d256-fp8", 32, 4, 256, "fp8", [9000, 4096], [16, 9], None, 4096),
     # bf16 at head_dim 256 runs producer/consumer wave pairs: 8 heads per tile
     ("verify-g8-d256-bf16", 32, 4, 256, "bf16", [9000, 4096], [16, 9], None, 4096),
+    # register-streaming kernel with two column tiles (3 rows x 8 heads) and
+    # with one q head per kv head
+    ("narrow-g8-d256", 32, 4, 256, "bf16", [7000, 300], [3, 2], None, 4096),
+    ("mha-d256-fp8", 4, 4, 256, "fp8", [3000, 8193], [2, 1], ["slab", "paged"], 4096),
 ]
 
 
