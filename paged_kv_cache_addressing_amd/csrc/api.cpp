@@ -161,18 +161,18 @@ struct RowTiling {
 // column count, so no wave holds a partial row and the workgroup's K/V
 // tiles serve as many q heads as that allows.
 RowTiling prefill_tiling(int32_t kv_dtype, int32_t head_dim, int32_t group) {
-  const int32_t cols = pa::prefill_columns(kv_dtype, head_dim);
+  const int32_t cols = pa::prefill_columns(kv_dtype, head_dim, false);
   int32_t hw = 1;
   for (int32_t d = 1; d <= group && d <= cols; ++d)
     if (group % d == 0 && cols % d == 0) hw = d;
-  return {hw, pa::prefill_wg_columns(kv_dtype, head_dim) / hw};
+  return {hw, pa::prefill_wg_columns(kv_dtype, head_dim, false) / hw};
 }
 
 // Decode streams with many columns: the largest divisor of the group that
 // fits the workgroup's columns (the whole group whenever it fits), so every
 // split's K/V is read by as few workgroups as possible.
 RowTiling wide_tiling(int32_t kv_dtype, int32_t head_dim, int32_t group) {
-  const int32_t cols = pa::prefill_wg_columns(kv_dtype, head_dim);
+  const int32_t cols = pa::prefill_wg_columns(kv_dtype, head_dim, true);
   int32_t hw = 1;
   for (int32_t d = 1; d <= group && d <= cols; ++d)
     if (group % d == 0) hw = d;

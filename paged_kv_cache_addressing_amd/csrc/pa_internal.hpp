@@ -14,10 +14,11 @@ int launch_decode_partials(const DecodeArgs& A, int kv_dtype, int head_dim, int 
                            hipStream_t st);
 int launch_decode_merge(const DecodeArgs& A, int head_dim, hipStream_t st);
 // MFMA columns ((row, q head) pairs) one column group of the row-tile
-// kernel covers (a wave, or a producer/consumer wave pair).
-int prefill_columns(int kv_dtype, int head_dim);
+// kernel covers (a wave, or a producer/consumer wave pair), in prefill or
+// in split mode.
+int prefill_columns(int kv_dtype, int head_dim, bool split);
 // MFMA columns one row-tile workgroup covers (all its column groups).
-int prefill_wg_columns(int kv_dtype, int head_dim);
+int prefill_wg_columns(int kv_dtype, int head_dim, bool split);
 int launch_prefill(const PrefillArgs& A, int kv_dtype, int head_dim, hipStream_t st);
 int launch_write_kv(const WriteArgs& A, int kv_dtype, int head_dim, hipStream_t st);
 int launch_page_copy(const PageCopyArgs& A, hipStream_t st);

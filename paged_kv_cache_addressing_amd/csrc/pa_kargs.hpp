@@ -17,21 +17,24 @@ constexpr int kMaxLaunchStreams = 32; // streams per kernel launch; calls are ch
 // columns sharing one set of K/V tiles.
 // Row-tile kernel shape.  A column group is the 16 * ntiles MFMA columns
 // that one wave holds, or, at head_dim 256, one producer/consumer wave pair
-// (the producer runs S and the softmax, the consumer P.V).
+// (the producer runs S and the softmax, the consumer P.V).  Split mode
+// (decode streams with many rows, e.g. 16 verify rows x 6 heads = 96
+// columns) uses two n-tiles per pair, prefill three (fewer LDS fragment
+// reads per product, 192 columns per workgroup).
 constexpr bool prefill_paired(int kv, int head_dim) { return (kv == 0 || kv == 1) && head_dim >= 256; }
 constexpr int prefill_waves(int head_dim) { return head_dim >= 256 ? 8 : 4; }
-constexpr int prefill_ntiles(int kv, int head_dim) {
-  return prefill_paired(kv, head_dim) ? 2 : head_dim >= 256 ? 1 : 3;
+constexpr int prefill_ntiles(int kv, int head_dim, bool split) {
+  return prefill_paired(kv, head_dim) ? (split ? 2 : 3) : head_dim >= 256 ? 1 : 3;
 }
 constexpr int prefill_groups(int kv, int head_dim) {
   return prefill_paired(kv, head_dim) ? prefill_waves(head_dim) / 2 : prefill_waves(head_dim);
 }
-// A workgroup's column count is the same for both KV dtypes, so a decode
-// plan (workspace and block counts) need not know the dtype.
-static_assert(prefill_groups(0, 256) * prefill_ntiles(0, 256) ==
-                  prefill_groups(1, 256) * prefill_ntiles(1, 256) &&
-              prefill_groups(0, 128) * prefill_ntiles(0, 128) ==
-                  prefill_groups(1, 128) * prefill_ntiles(1, 128),
+// A split-mode workgroup's column count is the same for both KV dtypes, so
+// a decode plan (workspace and block counts) need not know the dtype.
+static_assert(prefill_groups(0, 256) * prefill_ntiles(0, 256, true) ==
+                  prefill_groups(1, 256) * prefill_ntiles(1, 256, true) &&
+              prefill_groups(0, 128) * prefill_ntiles(0, 128, true) ==
+                  prefill_groups(1, 128) * prefill_ntiles(1, 128, true),
               "workgroup columns independent of the KV dtype");
 
 struct StreamArg {

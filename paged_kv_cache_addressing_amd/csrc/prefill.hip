@@ -89,7 +89,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, int voff, int s
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
 }
 
-template <int KV, int D>
+template <int KV, int D, bool SPLIT>
 __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const PrefillArgs A) {
   // A workgroup owns one kv head g, HW = heads_per_wg of its q heads (head
   // group hg) and a tile of rpt rows: its 4*16*NT columns, numbered
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   constexpr int KS = D / 32;            // QK k-steps
   constexpr int MD = D / 16;            // O^T m-tiles
   constexpr bool PAIR = prefill_paired(KV, D);  // producer/consumer wave pairs
-  constexpr int NT = prefill_ntiles(KV, D);  // 16-column n-tiles per column group
+  constexpr int NT = prefill_ntiles(KV, D, SPLIT);  // 16-column n-tiles per column group
   constexpr int NG = prefill_groups(KV, D);  // column groups per workgroup
   constexpr int NW = prefill_waves(D);   // waves per workgroup
   constexpr int NTH = 64 * NW;          // threads per workgroup
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   const int G = A.group;
   const int HW = A.heads_per_wg;
   const int rpt = A.rows_per_tile;
-  const bool split_mode = A.split_keys > 0;
+  constexpr bool split_mode = SPLIT;  // the host launches this instance iff split_keys > 0
 
   // Logical work item: (kv head, head group) major, then items (prefill:
   // row tiles longest first; split mode: (row tile, split) in order).  With
@@ -175,31 +175,45 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   // position, or (ancestor table) the stream's first row key
   const int mask_from = S.tree_mask ? S.first_pos : pos_first + 1;
 
-  // Columns of this wave.
-  int crow[NT], chead[NT], cpos[NT];
-  uint32_t canc[NT];  // ancestor word of the column's row (all ones: causal chain)
-  bool cok[NT];
-  v8bf qb[NT][KS];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int c = 16 * NT * cg + 16 * nt + n;
+  // Column nt of this wave: its q head, its row (absolute in the stream),
+  // whether the row is in the tile, and the last key it sees.  Recomputed
+  // where needed from an opaque copy of the lane index, so none of it stays
+  // in registers through the step loop.
+  struct Col {
+    int row, head, pos;
+    bool ok;
+  };
+  auto col = [&](int nt) -> Col {
+    int ln = n;
+    asm("" : "+v"(ln));
+    const int c = 16 * NT * cg + 16 * nt + ln;
     const int rl = c / HW;
-    chead[nt] = h0 + (c - rl * HW);
-    crow[nt] = row0 + rl;
-    cok[nt] = rl < rows_here;
-    cpos[nt] = cok[nt] ? S.first_pos + crow[nt] : pos_last;
-    canc[nt] = (S.tree_mask && cok[nt]) ? S.tree_mask[crow[nt]] : 0xFFFFFFFFu;
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(A.q) +
-                        ((int64_t)(S.row_offset + (cok[nt] ? crow[nt] : row0)) * A.n_q_heads +
-                         (cok[nt] ? chead[nt] : h0)) * D * 2;
+    Col k;
+    k.head = h0 + (c - rl * HW);
+    k.row = row0 + rl;
+    k.ok = rl < rows_here;
+    k.pos = k.ok ? S.first_pos + k.row : pos_last;
+    return k;
+  };
+  // Q^T fragments of this wave's columns (loaded by the waves that run the S
+  // product, inside their own copy of the step loop).
+  v8bf qb[NT][KS];
+  auto load_q = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = KV ? 64 * (ks >> 1) + 16 * a + 8 * (ks & 1) : 32 * ks + 8 * a;
-      v4u x = producer ? load16(qp + d0 * 2) : v4u{0, 0, 0, 0};
-      if (!cok[nt]) x = v4u{0, 0, 0, 0};
-      qb[nt][ks] = as_bf(x);
+    for (int nt = 0; nt < NT; ++nt) {
+      const Col k = col(nt);
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(A.q) +
+                          ((int64_t)(S.row_offset + (k.ok ? k.row : row0)) * A.n_q_heads +
+                           (k.ok ? k.head : h0)) * D * 2;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = KV ? 64 * (ks >> 1) + 16 * a + 8 * (ks & 1) : 32 * ks + 8 * a;
+        v4u x = load16(qp + d0 * 2);
+        if (!k.ok) x = v4u{0, 0, 0, 0};
+        qb[nt][ks] = as_bf(x);
+      }
     }
-  }
+  };
 
   v4u* const Kbase = lds;
   v4u* const Vbase = lds + NSLOT * KSLOT;
@@ -353,7 +367,10 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   auto mask = [&](int v, v4f (&Sx)[MT][NT]) {
     const int kabs0 = v * BK + 8 * a;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt) {
+      const Col k = col(nt);
+      // ancestor word of the column's row (all ones: causal chain)
+      const uint32_t anc = (S.tree_mask && k.ok) ? S.tree_mask[k.row] : 0xFFFFFFFFu;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -361,10 +378,11 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
           // branch-free: a select per logit (nested conditions here were
           // compiled into control flow that dropped the ancestor test)
           const int kabs = kabs0 + 4 * mt + i, rel = kabs - S.first_pos;
-          const bool anc_ok = (rel < 0) | (((canc[nt] >> (rel & 31)) & 1u) != 0u);
-          const bool vis = (kabs <= cpos[nt]) & anc_ok;
+          const bool anc_ok = (rel < 0) | (((anc >> (rel & 31)) & 1u) != 0u);
+          const bool vis = (kabs <= k.pos) & anc_ok;
           Sx[mt][nt][i] = vis ? Sx[mt][nt][i] : -INFINITY;
         }
+    }
   };
 
   // S(v+1) = K(v+1) Q^T on the matrix cores with the softmax of S(v) on the
@@ -629,12 +647,13 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   // Output of column n-tile nt with row sum l and running max m*c (log2
   // units).
   auto write_out = [&](int nt, float l, float mc) {
-    if (!cok[nt]) return;
+    const Col k = col(nt);
+    if (!k.ok) return;
     if (split_mode) {
       // Partial of (row, head, split): p was exp2(s*c - m_run*c), so the
       // split's m in log2 units is exactly m_run*c; o stays in stored-V units.
       const int64_t slot =
-          S.slot_base + ((int64_t)crow[nt] * A.n_q_heads + chead[nt]) * S.n_splits + split;
+          S.slot_base + ((int64_t)k.row * A.n_q_heads + k.head) * S.n_splits + split;
       // A rejected page id poisons m as a NaN bit pattern (this file is built
       // without NaN semantics, so no floating-point NaN is ever formed here).
       if (a == 0) {
@@ -649,7 +668,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
     }
     const float f = A.v_scale / l;
     uint16_t* dst =
-        A.out + ((int64_t)(S.row_offset + crow[nt]) * A.n_q_heads + chead[nt]) * D + 4 * a;
+        A.out + ((int64_t)(S.row_offset + k.row) * A.n_q_heads + k.head) * D + 4 * a;
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
       const v4f x = o[md][nt] * f;
@@ -668,6 +687,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   // producer) are free in its copy.
   auto run = [&](auto role) {
     constexpr int R = decltype(role)::value;
+    if constexpr (R != 1) load_q();
     // Prologue: K(v_lo), V(v_lo), K(v_lo+1) resident as bf16 (bf16 also has
     // K(v_lo+2), V(v_lo+1) in flight; fp8 has the codes of V(v_lo+1..v_lo+2)
     // and K(v_lo+2..v_lo+3) in flight); S(v_lo) computed; then the slot of
@@ -794,23 +814,30 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   }
 }
 
-template <int KV, int D>
+template <int KV, int D, bool SPLIT>
 static int launch_prefill_t(const PrefillArgs& A, hipStream_t st) {
   dim3 grid((unsigned)(A.total_tiles * A.cache.n_kv_heads * (A.group / A.heads_per_wg)));
-  hipLaunchKernelGGL((prefill_kernel<KV, D>), grid, dim3(64 * prefill_waves(D)), 0, st, A);
+  hipLaunchKernelGGL((prefill_kernel<KV, D, SPLIT>), grid, dim3(64 * prefill_waves(D)), 0, st, A);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-int prefill_columns(int kv_dtype, int head_dim) { return 16 * prefill_ntiles(kv_dtype, head_dim); }
-int prefill_wg_columns(int kv_dtype, int head_dim) {
-  return prefill_groups(kv_dtype, head_dim) * prefill_columns(kv_dtype, head_dim);
+int prefill_columns(int kv_dtype, int head_dim, bool split) {
+  return 16 * prefill_ntiles(kv_dtype, head_dim, split);
+}
+int prefill_wg_columns(int kv_dtype, int head_dim, bool split) {
+  return prefill_groups(kv_dtype, head_dim) * prefill_columns(kv_dtype, head_dim, split);
 }
 
 int launch_prefill(const PrefillArgs& A, int kv_dtype, int head_dim, hipStream_t st) {
-  if (kv_dtype == 0 && head_dim == 128) return launch_prefill_t<0, 128>(A, st);
-  if (kv_dtype == 0 && head_dim == 256) return launch_prefill_t<0, 256>(A, st);
-  if (kv_dtype == 1 && head_dim == 128) return launch_prefill_t<1, 128>(A, st);
-  if (kv_dtype == 1 && head_dim == 256) return launch_prefill_t<1, 256>(A, st);
+  const bool sp = A.split_keys > 0;
+  if (kv_dtype == 0 && head_dim == 128)
+    return sp ? launch_prefill_t<0, 128, true>(A, st) : launch_prefill_t<0, 128, false>(A, st);
+  if (kv_dtype == 0 && head_dim == 256)
+    return sp ? launch_prefill_t<0, 256, true>(A, st) : launch_prefill_t<0, 256, false>(A, st);
+  if (kv_dtype == 1 && head_dim == 128)
+    return sp ? launch_prefill_t<1, 128, true>(A, st) : launch_prefill_t<1, 128, false>(A, st);
+  if (kv_dtype == 1 && head_dim == 256)
+    return sp ? launch_prefill_t<1, 256, true>(A, st) : launch_prefill_t<1, 256, false>(A, st);
   return -7;
 }
 
