@@ -99,11 +99,13 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   const int krow = 8 * KK * (n >> 2) + (n & 3);
 
   // The wave's chunks, in order: its pages p_lo + wave, + NW, ..., each cut
-  // into CK-key chunks up to the split's end.  Two register sets alternate:
-  // the next chunk's K and V loads are issued before this chunk's products,
-  // so a wave always has a chunk of bytes in flight while it computes.  Each
-  // K/V byte is read once, so the loads are streaming (nontemporal).
-  auto load = [&](v4u (&kr)[KL], v4u (&vr)[MD], const PageTile& T, int c0) {
+  // into CK-key chunks up to the split's end.  Two register sets alternate,
+  // two chunks ahead: once the S^T products of chunk i have read its K
+  // registers they are refilled with the K of chunk i+2, and likewise V after
+  // the P.V products, so about one and a half chunks of bytes stay in flight
+  // while the wave computes.  Each K/V byte is read once, so the loads are
+  // streaming (nontemporal).
+  auto load_k = [&](v4u (&kr)[KL], const PageTile& T, int c0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint8_t* kp = T.k + (int64_t)(c0 + krow + 4 * mt) * D * ESZ;
@@ -115,12 +117,14 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
         for (int ks = 0; ks < KS; ++ks) kr[mt * KS + ks] = load16_stream(kp + (32 * ks + 8 * a) * 2);
       }
     }
-    // V block of this chunk (CK == 64/ESZ keys): D rows of 64 bytes.
+  };
+  // V block of a chunk (CK == 64/ESZ keys): D rows of 64 bytes.
+  auto load_v = [&](v4u (&vr)[MD], const PageTile& T, int c0) {
     const uint8_t* vb = T.v + (int64_t)c0 * D * ESZ + (8 * KK * a) * ESZ;
 #pragma unroll
     for (int md = 0; md < MD; ++md) vr[md] = load16_stream(vb + (16 * md + n) * 64);
   };
-  auto chunk = [&](v4u (&kr)[KL], v4u (&vr)[MD], int p, int c0) {
+  auto chunk = [&](v4u (&kr)[KL], v4u (&vr)[MD], int p, int c0, auto after_qk, auto after_pv) {
     v4f sacc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -137,6 +141,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
         sacc[mt] = mfma16(ka, qb[ks], sacc[mt]);
       }
     }
+    after_qk();
 
     // Online softmax for this lane's column over its 4*MT keys.
     const int kabs0 = p * kPage + c0 + 8 * KK * a;
@@ -200,6 +205,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
           va = as_bf(vr[md]);
         o[md] = mfma16(va, pb[kk], o[md]);
       }
+    after_pv();
   };
   // (p, c0) -> the wave's next chunk
   auto advance = [&](int& p, int& c0) {
@@ -209,42 +215,51 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
       c0 = 0;
     }
   };
+  // Chunks i (p0, c0), i+1 (p1, c1) and i+2 (p2, c2), with their page tiles;
+  // the page table is read once per page as a chunk first enters the queue.
   v4u krA[KL], vrA[MD], krB[KL], vrB[MD];
-  int p = p_lo + wave, c0 = 0;
-  PageTile T{};
-  if (p < p_hi) {
-    T = page_tile<D, ESZ>(S, A.cache, p, g);
-    bad |= !T.ok;
-    load(krA, vrA, T, c0);
+  int p0 = p_lo + wave, c0 = 0;
+  int p1 = p0, c1 = c0;
+  advance(p1, c1);
+  PageTile T0{}, T1{};
+  if (p0 < p_hi) {
+    T0 = page_tile<D, ESZ>(S, A.cache, p0, g);
+    bad |= !T0.ok;
+    load_k(krA, T0, c0);
+    load_v(vrA, T0, c0);
   }
-  // Issue the loads of the chunk after (p, c0) into (kr, vr); returns it.
-  auto prefetch = [&](v4u (&kr)[KL], v4u (&vr)[MD], int& pn, int& cn, PageTile& Tn) {
-    pn = p;
-    cn = c0;
-    advance(pn, cn);
-    Tn = T;
-    if (pn < p_hi) {
-      if (pn != p) {
-        Tn = page_tile<D, ESZ>(S, A.cache, pn, g);
-        bad |= !Tn.ok;
-      }
-      load(kr, vr, Tn, cn);
+  if (p1 < p_hi) {
+    T1 = T0;
+    if (p1 != p0) {
+      T1 = page_tile<D, ESZ>(S, A.cache, p1, g);
+      bad |= !T1.ok;
     }
+    load_k(krB, T1, c1);
+    load_v(vrB, T1, c1);
+  }
+  // Compute chunk i from (kr, vr), refilling them with chunk i+2.
+  auto run_chunk = [&](v4u (&kr)[KL], v4u (&vr)[MD]) {
+    int p2 = p1, c2 = c1;
+    advance(p2, c2);
+    PageTile T2 = T1;
+    const bool more = p2 < p_hi;
+    if (more && p2 != p1) {
+      T2 = page_tile<D, ESZ>(S, A.cache, p2, g);
+      bad |= !T2.ok;
+    }
+    chunk(kr, vr, p0, c0, [&] { if (more) load_k(kr, T2, c2); },
+          [&] { if (more) load_v(vr, T2, c2); });
+    p0 = p1;
+    c0 = c1;
+    T0 = T1;
+    p1 = p2;
+    c1 = c2;
+    T1 = T2;
   };
-  while (p < p_hi) {
-    int pn, cn;
-    PageTile Tn;
-    prefetch(krB, vrB, pn, cn, Tn);
-    chunk(krA, vrA, p, c0);
-    p = pn;
-    c0 = cn;
-    T = Tn;
-    if (p >= p_hi) break;
-    prefetch(krA, vrA, pn, cn, Tn);
-    chunk(krB, vrB, p, c0);
-    p = pn;
-    c0 = cn;
-    T = Tn;
+  while (p0 < p_hi) {
+    run_chunk(krA, vrA);
+    if (p0 >= p_hi) break;
+    run_chunk(krB, vrB);
   }
 
   // Per-column row sum across the four lane groups, in a fixed order.
