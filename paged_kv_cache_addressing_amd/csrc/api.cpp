@@ -554,7 +554,7 @@ int prepare_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n
     B.split_keys = split_keys;
     B.scale_log2 = scale_log2;
     B.v_scale = vs;
-    int32_t splits = 0, rows = 0, items = 0;
+    int32_t splits = 0, rows = 0, items = 0, full = 0;
     for (int32_t i : grp) {
       pa::StreamArg a = stream_arg(cache, streams[i]);
       a.n_splits = P.splits[i];
@@ -563,8 +563,12 @@ int prepare_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n
       rows += a.n_rows;
       A.s[A.n_streams++] = a;
       if (wide_stream(streams[i], group)) {
+        const int32_t tiles = (a.n_rows + W.rows - 1) / W.rows;
         a.block_begin = items;
-        items += (a.n_rows + W.rows - 1) / W.rows * a.n_splits;
+        items += tiles * a.n_splits;
+        a.full_begin = full;
+        full += tiles * (a.n_keys / split_keys);
+        a.part_begin = -1;
         B.s[B.n_streams++] = a;
       } else {
         a.block_begin = splits;
@@ -572,9 +576,26 @@ int prepare_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n
         D.narrow.s[D.narrow.n_streams++] = a;
       }
     }
+    // Row-tile split mode runs one workgroup per CU, so the order of its
+    // items decides the tail: every whole split first, then the streams'
+    // shorter last splits, longest first (ties in stream order).
+    {
+      std::vector<int32_t> order;
+      for (int32_t j = 0; j < B.n_streams; ++j)
+        if (B.s[j].n_keys % split_keys != 0) order.push_back(j);
+      std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+        return B.s[x].n_keys % split_keys > B.s[y].n_keys % split_keys;
+      });
+      int32_t rank = full;
+      for (int32_t j : order) {
+        B.s[j].part_begin = rank - full;
+        rank += (B.s[j].n_rows + W.rows - 1) / W.rows;
+      }
+    }
     A.total_rows = rows;
     D.narrow.total_splits = splits;
     B.total_tiles = items;
+    B.full_tiles = full;
     launches.push_back(D);
   }
   return PA_OK;

@@ -46,6 +46,8 @@ struct StreamArg {
   int32_t n_splits;     // decode: ceil(n_keys / split_keys)
   int32_t block_begin;  // decode: first split of the stream in the launch; prefill: first row tile
   int32_t row_begin;    // first row of the stream in the launch's row numbering
+  int32_t full_begin;   // row-tile split mode: first of the stream's whole-split items
+  int32_t part_begin;   // row-tile split mode: rank of its short last split's items, or -1
   int64_t slot_base;    // decode: workspace slot of (row 0, head 0, split 0)
   const int32_t* page_table;  // paged: device page ids
   uint8_t* k_base;      // paged: pool K base; slab: slab K base
@@ -98,6 +100,8 @@ struct PrefillArgs {
   int32_t rows_per_tile;  // rows a workgroup covers: floor(4 * columns per wave / heads_per_wg)
   int32_t split_keys;     // 0: prefill; > 0: split-K partials of this many keys
   int32_t xcd_remap;      // 1: map blocks so each XCD runs one contiguous range
+  int32_t full_tiles;     // split mode: items of whole splits (per head group)
+  int32_t pad0;
   float scale_log2;
   float v_scale;
   StreamArg s[kMaxLaunchStreams];

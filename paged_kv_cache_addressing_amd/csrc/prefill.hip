@@ -147,15 +147,45 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   const int nb = gridDim.x;
   const int L = A.xcd_remap ? (int)(blockIdx.x % 8) * (nb / 8) + (int)(blockIdx.x / 8)
                             : (int)blockIdx.x;
-  const int hgrp = L / A.total_tiles;      // kv head * (G / HW) + head group
+  // Split mode: blocks [0, NH * F) are the whole splits (head group major,
+  // then stream, row tile, split); the rest are the streams' shorter last
+  // splits, longest first, all head groups of one before the next.
+  int hgrp, si, tile, split;  // hgrp = kv head * (G / HW) + head group
+  if (split_mode) {
+    const int NH = nb / A.total_tiles;
+    const int F = A.full_tiles;
+    if (L < NH * F) {
+      hgrp = L / F;
+      const int r = L - hgrp * F;
+      si = 0;
+      for (int i = 1; i < A.n_streams; ++i)
+        if (r >= A.s[i].full_begin) si = i;
+      const int nf = A.s[si].n_keys / A.split_keys;
+      const int local = r - A.s[si].full_begin;
+      tile = local / nf;
+      split = local - tile * nf;
+    } else {
+      const int j = L - NH * F;
+      hgrp = j % NH;
+      const int r = j / NH;
+      si = 0;
+      for (int i = 0; i < A.n_streams; ++i) {
+        const int pb = A.s[i].part_begin;
+        if (pb >= 0 && r >= pb && r < pb + (A.s[i].n_rows + rpt - 1) / rpt) si = i;
+      }
+      tile = r - A.s[si].part_begin;
+      split = A.s[si].n_splits - 1;
+    }
+  } else {
+    hgrp = L / A.total_tiles;
+    const int it = A.total_tiles - 1 - L % A.total_tiles;
+    si = find_stream<0>(A.s, A.n_streams, it);
+    tile = it - A.s[si].block_begin;
+    split = 0;
+  }
   const int g = hgrp / (G / HW);
   const int h0 = g * G + (hgrp % (G / HW)) * HW;
-  const int it = split_mode ? L % A.total_tiles : A.total_tiles - 1 - L % A.total_tiles;
-  const int si = find_stream<0>(A.s, A.n_streams, it);
   const StreamArg& S = A.s[si];
-  const int local = it - S.block_begin;
-  const int tile = split_mode ? local / S.n_splits : local;
-  const int split = split_mode ? local - tile * S.n_splits : 0;
   const int row0 = tile * rpt;
   const int rows_here = min(rpt, S.n_rows - row0);
   const int pos_first = S.first_pos + row0;
