@@ -141,12 +141,24 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   constexpr bool split_mode = SPLIT;  // the host launches this instance iff split_keys > 0
 
   // Logical work item: (kv head, head group) major, then items (prefill:
-  // row tiles longest first; split mode: (row tile, split) in order).  With
-  // the remap, the blocks one XCD runs (blockIdx % 8 picks the XCD) form one
-  // contiguous logical range, i.e. one kv head, whose K/V then hit in L2.
+  // row tiles longest first; split mode: see below).  With the remap, the
+  // blocks one XCD runs (blockIdx % 8 picks the XCD) come from one head
+  // group, whose K/V then hit in that XCD's L2.  When a head group's tiles
+  // fill m whole XCDs, its tiles, longest first, are dealt to them in
+  // snake order (0 1 .. m-1, m-1 .. 1 0, ...), so the m XCDs get equal
+  // sums of work rather than the longest tiles going to the first of them.
   const int nb = gridDim.x;
-  const int L = A.xcd_remap ? (int)(blockIdx.x % 8) * (nb / 8) + (int)(blockIdx.x / 8)
-                            : (int)blockIdx.x;
+  int L = (int)blockIdx.x;
+  if (A.xcd_remap) {
+    const int x = (int)(blockIdx.x % 8), sl = (int)(blockIdx.x / 8), C = nb / 8;
+    if (!split_mode && A.total_tiles % C == 0) {
+      const int m = A.total_tiles / C;
+      const int off = x % m;
+      L = (x / m) * A.total_tiles + sl * m + ((sl & 1) ? m - 1 - off : off);
+    } else {
+      L = x * C + sl;
+    }
+  }
   // Split mode: blocks [0, NH * F) are the whole splits (head group major,
   // then stream, row tile, split); the rest are the streams' shorter last
   // splits, longest first, all head groups of one before the next.
