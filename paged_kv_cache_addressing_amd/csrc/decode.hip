@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   __shared__ int sh_bad[NW];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: SGPR arithmetic
   const int n = lane & 15;
   const int a = lane >> 4;
   const int g = blockIdx.y;
@@ -88,6 +88,19 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   const int k_hi = min(k_lo + A.split_keys, S.n_keys);
   const int p_lo = k_lo / kPage;
   const int p_hi = (k_hi + kPage - 1) / kPage;
+  // The waves walk the split's pages in the order p_lo + wave, + NW, ...,
+  // read through a rotation by the split index: physical page
+  // p_lo + (p - p_lo + split) mod (pages of the split).  Contiguous slabs
+  // put the splits of a stream at regular strides, and without it every
+  // workgroup would touch the same offsets of its split at the same time.
+  // The rotation depends on the split alone, never on the batch.
+  const int np = p_hi - p_lo;
+  const int rot = np > 0 ? split % np : 0;
+  auto phys = [&](int p) {
+    int v = p - p_lo + rot;
+    if (v >= np) v -= np;
+    return p_lo + v;
+  };
 
   v4f o[MD];
 #pragma unroll
@@ -147,18 +160,27 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
     const int kabs0 = p * kPage + c0 + 8 * KK * a;
     const bool need_mask = p * kPage + c0 + CK - 1 >= mask_from;
     float sv[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[mt][i] = sacc[mt][i] * A.scale_log2;
+    // Only chunks that reach a row's own keys can hold a masked key; the
+    // test is wave-uniform, so the mask is skipped as a whole elsewhere.
+    if (need_mask) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kabs = kabs0 + 4 * mt + i, rel = kabs - S.first_pos;
+          const bool vis = (kabs <= pos) & ((rel < 0) | (((anc >> (rel & 31)) & 1u) != 0u));
+          sv[mt][i] = vis ? sv[mt][i] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = sacc[mt][i] * A.scale_log2;
-        const int kabs = kabs0 + 4 * mt + i, rel = kabs - S.first_pos;
-        const bool vis = (kabs <= pos) & ((rel < 0) | (((anc >> (rel & 31)) & 1u) != 0u));
-        if (need_mask && !vis) v = -INFINITY;
-        sv[mt][i] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[mt][i]);
     mx = rows4_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -210,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   // (p, c0) -> the wave's next chunk
   auto advance = [&](int& p, int& c0) {
     c0 += CK;
-    if (c0 >= min(kPage, k_hi - p * kPage)) {
+    if (c0 >= min(kPage, k_hi - phys(p) * kPage)) {
       p += NW;
       c0 = 0;
     }
@@ -223,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   advance(p1, c1);
   PageTile T0{}, T1{};
   if (p0 < p_hi) {
-    T0 = page_tile<D, ESZ>(S, A.cache, p0, g);
+    T0 = page_tile<D, ESZ>(S, A.cache, phys(p0), g);
     bad |= !T0.ok;
     load_k(krA, T0, c0);
     load_v(vrA, T0, c0);
@@ -231,7 +253,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   if (p1 < p_hi) {
     T1 = T0;
     if (p1 != p0) {
-      T1 = page_tile<D, ESZ>(S, A.cache, p1, g);
+      T1 = page_tile<D, ESZ>(S, A.cache, phys(p1), g);
       bad |= !T1.ok;
     }
     load_k(krB, T1, c1);
@@ -244,10 +266,10 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
     PageTile T2 = T1;
     const bool more = p2 < p_hi;
     if (more && p2 != p1) {
-      T2 = page_tile<D, ESZ>(S, A.cache, p2, g);
+      T2 = page_tile<D, ESZ>(S, A.cache, phys(p2), g);
       bad |= !T2.ok;
     }
-    chunk(kr, vr, p0, c0, [&] { if (more) load_k(kr, T2, c2); },
+    chunk(kr, vr, phys(p0), c0, [&] { if (more) load_k(kr, T2, c2); },
           [&] { if (more) load_v(vr, T2, c2); });
     p0 = p1;
     c0 = c1;
