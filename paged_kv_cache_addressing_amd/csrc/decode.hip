@@ -326,53 +326,81 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
 
 // out[row][h] = v_scale * sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j, in
 // split order j = 0, 1, ...; a wholly masked split (m_j = -inf) weighs 0.
+// One block per (row, q head), thread d owning dim d.  M is reduced once for
+// the block; then, for each run of up to MB splits, the weights 2^(m_j - M)
+// and l_j go to LDS and every thread streams its dim of o_j, JB splits of
+// loads in flight at a time.  All sums run in split order, so the result
+// does not depend on how the splits are batched.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs A) {
+  constexpr int NT = D;    // threads per block
+  constexpr int MB = NT;   // splits per LDS run
+  constexpr int JB = 16;   // o_j loads in flight per thread
+  __shared__ float sh_w[MB];
+  __shared__ float sh_l[MB];
+  __shared__ float sh_red[NT / 64];
+  __shared__ int sh_bad[NT / 64];
   const int row = blockIdx.x;
   const int h = blockIdx.y;
+  const int t = threadIdx.x;
   const int si = find_stream<1>(A.s, A.n_streams, row);
   const StreamArg& S = A.s[si];
   const int r = row - S.row_begin;
   const int ns = S.n_splits;
   const int64_t slot0 = S.slot_base + ((int64_t)r * A.n_q_heads + h) * ns;
   const float* ml = A.ws_ml + 2 * slot0;
-  // Loads are batched JB splits at a time so their latencies overlap; the
-  // sums still run in split order.
-  constexpr int JB = 8;
-  float M = -INFINITY;
+
+  // M = max_j m_j over the whole block (max is exact in any order); a NaN m
+  // marks a partial computed from a rejected page id.
+  float mx = -INFINITY;
   bool bad = false;
-  for (int j0 = 0; j0 < ns; j0 += JB) {
-    float mb[JB];
-#pragma unroll
-    for (int u = 0; u < JB; ++u) mb[u] = j0 + u < ns ? ml[2 * (j0 + u)] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < JB; ++u) {
-      bad |= mb[u] != mb[u];
-      M = fmaxf(M, mb[u]);
-    }
+  for (int j = t; j < ns; j += NT) {
+    const float m = ml[2 * j];
+    bad |= m != m;
+    mx = fmaxf(mx, m);
   }
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int j0 = 0; j0 < ns; j0 += JB) {
-      float ob[JB], mb[JB], lb[JB];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  const bool wbad = __any(bad);
+  if ((t & 63) == 0) {
+    sh_red[t >> 6] = mx;
+    sh_bad[t >> 6] = wbad ? 1 : 0;
+  }
+  __syncthreads();
+  float M = sh_red[0];
+  bool any_bad = sh_bad[0] != 0;
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) {
+    M = fmaxf(M, sh_red[w]);
+    any_bad |= sh_bad[w] != 0;
+  }
+
+  float num = 0.f, den = 0.f;
+  const float* op = A.ws_o + slot0 * D + t;
+  for (int j0 = 0; j0 < ns; j0 += MB) {
+    const int nj = min(MB, ns - j0);
+    __syncthreads();  // the previous run's weights are consumed
+    if (t < nj) {
+      const float m = ml[2 * (j0 + t)];
+      sh_w[t] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      sh_l[t] = ml[2 * (j0 + t) + 1];
+    }
+    __syncthreads();
+    for (int jb = 0; jb < nj; jb += JB) {
+      float ob[JB];
+#pragma unroll
+      for (int u = 0; u < JB; ++u) ob[u] = jb + u < nj ? op[(int64_t)(j0 + jb + u) * D] : 0.f;
 #pragma unroll
       for (int u = 0; u < JB; ++u) {
-        const bool in = j0 + u < ns;
-        ob[u] = in ? A.ws_o[(slot0 + j0 + u) * D + d] : 0.f;
-        mb[u] = in ? ml[2 * (j0 + u)] : -INFINITY;
-        lb[u] = in ? ml[2 * (j0 + u) + 1] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < JB; ++u) {
-        if (j0 + u >= ns) break;
-        const float w = mb[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb[u] - M);
+        if (jb + u >= nj) break;
+        const float w = sh_w[jb + u];
         num += w * ob[u];
-        den += w * lb[u];
+        den += w * sh_l[jb + u];
       }
     }
-    const float res = bad ? __builtin_nanf("") : num / den * A.v_scale;
-    A.out[((int64_t)(S.row_offset + r) * A.n_q_heads + h) * D + d] = f2bf(res);
   }
+  const float res = any_bad ? __builtin_nanf("") : num / den * A.v_scale;
+  A.out[((int64_t)(S.row_offset + r) * A.n_q_heads + h) * D + t] = f2bf(res);
 }
 
 template <int KV, int D>
