@@ -392,6 +392,7 @@ def main():
                 sec[name]["traffic"] = traffic_for("prefill_kernel<fp8,256> split", "config5")
             else:
                 sec[name]["kernel"] = "decode_partial_kernel<fp8,256>"
+                sec[name]["traffic"] = traffic_for("decode_partial_kernel<fp8,256>", "config3")
             del w, res, out
             torch.cuda.empty_cache()
         line["secondary"] = sec
