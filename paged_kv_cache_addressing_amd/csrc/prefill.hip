@@ -119,8 +119,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   constexpr int KST = KF * 64 / 2;
   constexpr int VST = VF * 64 / 2;
   constexpr int NSTG = 3;
-  constexpr int K8PW = KST / NTH;       // fp8 DMAs per wave per step
-  constexpr int V8PW = VST / NTH;
+  static_assert(KST % (64 * NW) == 0 && VST % (64 * NW) == 0, "fp8 entries per loader wave");
   static_assert(kPage % BK == 0, "a step never straddles two pages");
 
   // Paired waves hand P (bf16, fragment order) and the rescale factors from
@@ -337,40 +336,56 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   // converts it; the conversion to bf16 fragment order then runs one step
   // ahead of use (K two steps).  Every E4M3FN value is a bf16 value, so the
   // conversion is exact.
+  //
+  // Loader waves.  Normally all NW waves share the staging entries.  In
+  // split mode, when the last column group holds no column (96 verify
+  // columns in 128), its two waves are the only loaders: they issue every DMA, wait for
+  // it and convert it, and the column-holding waves only compute and pass
+  // the barriers.  Loader wave li of NL takes K entry groups li, li + NL, ...
+  // and V entries (li * 64 + lane) + 64 NL i.
+  const bool ded = SPLIT && KV == 1 && PAIR && (NG - 1) * 16 * NT >= rows_here * HW;
+  const bool loader = !ded || cg == NG - 1;
+  const int li = ded ? (producer ? 0 : 1) : wave;
+  typedef std::integral_constant<int, NW> AllLoad;
+  typedef std::integral_constant<int, 2> PairLoad;
   v4u* const Sbase = lds + NSLOT * KSLOT + NVSLOT * VSLOT;
-  auto dma8_k = [&](int v, int sl) {
+  auto dma8_k = [&](int v, int sl, auto nl) __attribute__((always_inline)) {
+    constexpr int NL = decltype(nl)::value;
     const PageTile& T = page_k(v);
     const auto rs = tile_rsrc(T.k, kPage * D);
     const int soff = (v & 7) * BK * D;
     v4u* dst = Sbase + sl * (KST + VST);
 #pragma unroll
-    for (int i = 0; i < K8PW; ++i) {
+    for (int i = 0; i < KST / 64 / NL; ++i) {
       // entry fp*64 + lane: 16 dims (two QK k-steps) of one S^T row
-      const int fp = NW * i + wave, mt = fp / (KS / 2), kq = fp % (KS / 2);
+      const int fp = NL * i + li, mt = fp / (KS / 2), kq = fp % (KS / 2);
       const int off = (krow + 4 * mt) * D + 64 * kq + 16 * a;
       dma16(rs, off, soff, dst + fp * 64);
     }
   };
-  auto dma8_v = [&](int v, int sl) {
+  auto dma8_v = [&](int v, int sl, auto nl) __attribute__((always_inline)) {
+    constexpr int NL = decltype(nl)::value;
     const PageTile& T = page_v(v);
     const int o = (v & 7) * BK;
     const auto rs = tile_rsrc(T.v, kPage * D);
     v4u* dst = Sbase + sl * (KST + VST) + KST;
 #pragma unroll
-    for (int i = 0; i < V8PW; ++i) {
+    for (int i = 0; i < VST / 64 / NL; ++i) {
       // entry q: 16 keys (half h of the step) of dim 16*md + dl
-      const int q = i * NTH + tid, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
+      const int q = i * 64 * NL + li * 64 + lane, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
       const int off = v_off<D, ESZ>(o + 16 * h, 16 * md + dl);
       dma16(rs, off, 0, dst + (q >> 6) * 64);
     }
   };
-  auto convert_fp8 = [&](int vk, int stk, int slk, int vv, int stv, int slv, auto may_tail) {
+  auto convert_fp8 = [&](int vk, int stk, int slk, int vv, int stv, int slv, auto may_tail,
+                         auto nl) __attribute__((always_inline)) {
+    constexpr int NL = decltype(nl)::value;
     if (vk >= 0) {
       const v4u* St = Sbase + stk * (KST + VST);
       v4u* Ls = Kbase + slk * KSLOT;
 #pragma unroll
-      for (int i = 0; i < K8PW; ++i) {
-        const int fp = NW * i + wave, mt = fp / (KS / 2), kq = fp % (KS / 2);
+      for (int i = 0; i < KST / 64 / NL; ++i) {
+        const int fp = NL * i + li, mt = fp / (KS / 2), kq = fp % (KS / 2);
         const int f0 = mt * KS + 2 * kq;
         const v4u x = St[fp * 64 + lane];
         Ls[f0 * 64 + lane] = __builtin_bit_cast(v4u, fp8x8_to_bf16(x[0], x[1]));
@@ -382,8 +397,8 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       v4u* Ls = Vbase + slv * VSLOT;
       const bool tail = decltype(may_tail)::value && vv * BK + BK > n_keys_t;
 #pragma unroll
-      for (int i = 0; i < V8PW; ++i) {
-        const int q = i * NTH + tid, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
+      for (int i = 0; i < VST / 64 / NL; ++i) {
+        const int q = i * 64 * NL + li * 64 + lane, md = q >> 5, dl = q & 15, h = (q >> 4) & 1;
         v4u x = St[q];
         if (tail) x = keep_first_b(x, n_keys_t - (vv * BK + 16 * h));
         Ls[md * 64 + 32 * h + dl] = __builtin_bit_cast(v4u, fp8x8_to_bf16(x[0], x[1]));
@@ -567,7 +582,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   auto kslot = [&](int u) { return (u - v_lo) % NSLOT; };
   auto vslot = [&](int u) { return (u - v_lo) % NVSLOT; };
   // DMAs of step v; returns how many bf16 tiles were issued (0, 1 = V, 2).
-  auto issue = [&](int v, auto fast, auto ph) -> int {
+  auto issue = [&](int v, auto fast, auto ph) __attribute__((always_inline)) -> int {
     constexpr bool FAST = decltype(fast)::value;
     const int r0 = ph % 3, r1 = (ph + 1) % 3;  // staging of v+3, v+4
     int issued = 0;
@@ -575,23 +590,31 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       if (FAST || v + 2 < v_hi) { dma_v(v + 2, vslot(v + 2)); issued = 1; }
       if (FAST || v + 3 < v_hi) { dma_k(v + 3, kslot(v + 3)); issued = 2; }
     } else {
-      if (FAST || v + 4 < v_hi) dma8_k(v + 4, r1);
-      if (FAST || v + 3 < v_hi) dma8_v(v + 3, r0);
-      // Then convert K(v+2) and V(v+1) (staging positions r2 and r1) into
-      // their bf16 slots at the start of the step, so the conversion
-      // overlaps this step's products on the SIMD's other wave; barrier v
-      // publishes them.  Their codes have landed once at most the DMAs
-      // issued in steps v-1 and v (K(v+3), V(v+2), K(v+4), V(v+3), those
-      // that exist) remain.
-      const int r2 = (ph + 2) % 3;
-      const int r = v_hi - 1 - v;
-      if (FAST || r >= 4) wait_vmem<2 * (K8PW + V8PW)>();
-      else if (r == 3) wait_vmem<K8PW + 2 * V8PW>();
-      else if (r == 2) wait_vmem<V8PW>();
-      else wait_vmem<0>();
-      if (FAST) convert_fp8(v + 2, r2, kslot(v + 2), v + 1, r1, vslot(v + 1), std::false_type{});
-      else convert_fp8(v + 2 < v_hi ? v + 2 : -1, r2, kslot(v + 2), v + 1 < v_hi ? v + 1 : -1, r1,
-                       vslot(v + 1), std::true_type{});
+      auto load = [&](auto nl) __attribute__((always_inline)) {
+        constexpr int NL = decltype(nl)::value;
+        constexpr int K8 = KST / 64 / NL, V8 = VST / 64 / NL;  // DMAs per lane per step
+        if (FAST || v + 4 < v_hi) dma8_k(v + 4, r1, nl);
+        if (FAST || v + 3 < v_hi) dma8_v(v + 3, r0, nl);
+        // Then convert K(v+2) and V(v+1) (staging positions r2 and r1) into
+        // their bf16 slots at the start of the step, so the conversion
+        // overlaps this step's products on the SIMD's other wave; barrier v
+        // publishes them.  Their codes have landed once at most the DMAs
+        // issued in steps v-1 and v (K(v+3), V(v+2), K(v+4), V(v+3), those
+        // that exist) remain.
+        const int r2 = (ph + 2) % 3;
+        const int r = v_hi - 1 - v;
+        if (FAST || r >= 4) wait_vmem<2 * (K8 + V8)>();
+        else if (r == 3) wait_vmem<K8 + 2 * V8>();
+        else if (r == 2) wait_vmem<V8>();
+        else wait_vmem<0>();
+        if (FAST)
+          convert_fp8(v + 2, r2, kslot(v + 2), v + 1, r1, vslot(v + 1), std::false_type{}, nl);
+        else
+          convert_fp8(v + 2 < v_hi ? v + 2 : -1, r2, kslot(v + 2), v + 1 < v_hi ? v + 1 : -1, r1,
+                      vslot(v + 1), std::true_type{}, nl);
+      };
+      if (!ded) load(AllLoad{});
+      else if (loader) load(PairLoad{});
     }
     return issued;
   };
@@ -747,18 +770,22 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
         else if (n_st > 1) wait_vmem<VPW>();
         else wait_vmem<0>();
       } else {
-        dma8_k(v_lo, 0);
-        dma8_v(v_lo, 0);
-        if (n_st > 1) dma8_k(v_lo + 1, 1);
-        wait_vmem<0>();
-        convert_fp8(v_lo, 0, 0, v_lo, 0, 0, std::true_type{});
-        if (n_st > 1) convert_fp8(v_lo + 1, 1, 1, -1, 0, 0, std::true_type{});
-        // the staging reads above finish before K(v_lo+3) reuses K(v_lo)'s entries
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (n_st > 1) dma8_v(v_lo + 1, 1);
-        if (n_st > 2) dma8_k(v_lo + 2, 2);
-        if (n_st > 2) dma8_v(v_lo + 2, 2);
-        if (n_st > 3) dma8_k(v_lo + 3, 0);
+        auto prologue = [&](auto nl) __attribute__((always_inline)) {
+          dma8_k(v_lo, 0, nl);
+          dma8_v(v_lo, 0, nl);
+          if (n_st > 1) dma8_k(v_lo + 1, 1, nl);
+          wait_vmem<0>();
+          convert_fp8(v_lo, 0, 0, v_lo, 0, 0, std::true_type{}, nl);
+          if (n_st > 1) convert_fp8(v_lo + 1, 1, 1, -1, 0, 0, std::true_type{}, nl);
+          // the staging reads above finish before K(v_lo+3) reuses K(v_lo)'s entries
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          if (n_st > 1) dma8_v(v_lo + 1, 1, nl);
+          if (n_st > 2) dma8_k(v_lo + 2, 2, nl);
+          if (n_st > 2) dma8_v(v_lo + 2, 2, nl);
+          if (n_st > 3) dma8_k(v_lo + 3, 0, nl);
+        };
+        if (!ded) prologue(AllLoad{});
+        else if (loader) prologue(PairLoad{});
       }
       __syncthreads();
       if (KV == 0 && v_lo * BK + BK > n_keys_t) {
@@ -834,11 +861,16 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
           }
         }
       }
+      // With loader waves only they looked pages up: the producer of the
+      // loader pair passes on whether a page id was rejected.
+      if (ded && cg == NG - 1 && lane == 0)
+        reinterpret_cast<int*>(lds)[NG * NT * 32] = bad ? 1 : 0;
       __syncthreads();
     } else if constexpr (R == 1) {
       const float* X = reinterpret_cast<const float*>(lds);
       __syncthreads();
       if (!wave_active) return;
+      if (ded) bad |= reinterpret_cast<const int*>(lds)[NG * NT * 32] != 0;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         write_out(nt, X[(cg * NT + nt) * 32 + n], X[(cg * NT + nt) * 32 + 16 + n]);
