@@ -100,6 +100,9 @@ DECODE_CASES = [
     ("verify-fp8-masked-split", 24, 4, 256, "fp8", [4100, 6000, 4096 + 16], [16, 16, 16],
      None, 4096),
     ("small-split", 6, 1, 256, "bf16", [3000], [5], None, 256),
+    # more than 256 splits per row (the merge stages split weights 256 at a
+    # time) and one-page splits (the page walk's rotation is the identity)
+    ("many-splits", 8, 2, 128, "bf16", [70000, 600], [1, 2], ["paged", "slab"], 256),
     # verify rows on the LDS-shared row-tile kernel in split mode
     ("verify-bf16-d256-mixed", 24, 4, 256, "bf16", [3 * 4096 + 5, 9000, 316], [16, 16, 16],
      ["paged", "slab", "paged"], 4096),
