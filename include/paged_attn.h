@@ -291,6 +291,8 @@ typedef struct pa_decode_plan {
   int32_t partial_blocks;    /* workgroups of all partial kernels */
   int32_t merge_blocks;      /* workgroups of the merge kernel(s) */
   int32_t wide_blocks;       /* of partial_blocks: those of the LDS-shared row-tile kernel */
+  int32_t narrow_splits_per_wg; /* consecutive splits a register-streaming workgroup computes
+                                   (largest over launch groups; 0 when there is none) */
   size_t workspace_bytes;
 } pa_decode_plan;
 

@@ -61,7 +61,7 @@ class pa_decode_plan(C.Structure):
     _fields_ = [("n_launch_groups", C.c_int32), ("total_splits", C.c_int32),
                 ("col_tiles", C.c_int32), ("partial_blocks", C.c_int32),
                 ("merge_blocks", C.c_int32), ("wide_blocks", C.c_int32),
-                ("workspace_bytes", C.c_size_t)]
+                ("narrow_splits_per_wg", C.c_int32), ("workspace_bytes", C.c_size_t)]
 
 
 _lib = None

@@ -189,6 +189,21 @@ bool wide_stream(const pa_stream& t, int32_t group) {
   return (int64_t)t.n_rows * group > kWideColumns;
 }
 
+// Compute units of a gfx950 device (MI355X / MI350X).
+constexpr int64_t kComputeUnits = 256;
+
+// Consecutive splits of one (stream, kv head) that a register-streaming
+// decode workgroup computes.  Once the narrow launch needs two or more rounds
+// of workgroups, splits are grouped so that about one round remains: each
+// workgroup then starts once and keeps its loads flowing across the split
+// boundaries.  Grouping needs a split's pages to divide evenly over the four
+// waves, so that every split is walked exactly as by a workgroup of its own
+// (the partials do not depend on the grouping).
+int32_t narrow_splits_per_wg(int64_t blocks_one_split, int32_t split_keys) {
+  if (split_keys % (4 * kPage) != 0 || blocks_one_split < 2 * kComputeUnits) return 1;
+  return (int32_t)((blocks_one_split + kComputeUnits - 1) / kComputeUnits);
+}
+
 // Column tiles of the register-streaming partial kernel for a launch group:
 // enough for its widest narrow stream.
 int32_t col_tiles_of(const pa_stream* s, const std::vector<int32_t>& grp, int32_t group) {
@@ -477,8 +492,15 @@ int paged_attn_decode_plan(const pa_stream* streams, int32_t n_streams, int32_t 
       }
       const int32_t ct = col_tiles_of(streams, grp, group);
       const int32_t wb = wide_items * n_kv_heads * (group / W.heads);
+      const int32_t spw =
+          narrow_splits_per_wg((int64_t)narrow_splits * ct * n_kv_heads, split_keys);
+      int32_t narrow_items = 0;
+      for (int32_t i : grp)
+        if (!wide_stream(streams[i], group)) narrow_items += (P.splits[i] + spw - 1) / spw;
       plan->col_tiles = std::max(plan->col_tiles, ct);
-      plan->partial_blocks += narrow_splits * ct * n_kv_heads + wb;
+      if (narrow_splits > 0)
+        plan->narrow_splits_per_wg = std::max(plan->narrow_splits_per_wg, spw);
+      plan->partial_blocks += narrow_items * ct * n_kv_heads + wb;
       plan->wide_blocks += wb;
       plan->merge_blocks += tr * n_q_heads;
     }
@@ -571,11 +593,19 @@ int prepare_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n
         a.part_begin = -1;
         B.s[B.n_streams++] = a;
       } else {
-        a.block_begin = splits;
         splits += a.n_splits;
         D.narrow.s[D.narrow.n_streams++] = a;
       }
     }
+    // narrow workgroup items: runs of spw consecutive splits per stream
+    const int32_t spw = narrow_splits_per_wg(
+        (int64_t)splits * A.col_tiles * cache->n_kv_heads, split_keys);
+    int32_t items_n = 0;
+    for (int32_t j = 0; j < D.narrow.n_streams; ++j) {
+      D.narrow.s[j].block_begin = items_n;
+      items_n += (D.narrow.s[j].n_splits + spw - 1) / spw;
+    }
+    D.narrow.splits_per_wg = spw;
     // Row-tile split mode runs one workgroup per CU, so the order of its
     // items decides the tail: every whole split first, then the streams'
     // shorter last splits, longest first (ties in stream order).
@@ -593,7 +623,7 @@ int prepare_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_t n
       }
     }
     A.total_rows = rows;
-    D.narrow.total_splits = splits;
+    D.narrow.total_items = items_n;
     B.total_tiles = items;
     B.full_tiles = full;
     launches.push_back(D);

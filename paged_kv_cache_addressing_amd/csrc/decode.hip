@@ -3,9 +3,10 @@
 // Decode is a split partial followed by a merge (TensorFold issue #1344,
 // "Mechanism"); the decode tiles read key rows through the page table, one
 // lookup per page (pull request #2011, "What this changes").  One workgroup
-// owns one (stream, 4096-key split, kv head, 16-column tile); its four waves
-// take the split's pages round-robin and are combined in fixed wave order,
-// so the partial of a split depends on that split's keys and queries alone.
+// owns splits_per_wg consecutive 4096-key splits of one (stream, kv head,
+// 16-column tile); its four waves take each split's pages round-robin and
+// are combined in fixed wave order, so the partial of a split depends on
+// that split's keys and queries alone, whichever workgroup computes it.
 //
 // MFMA mapping (v_mfma_f32_16x16x32_bf16, wave64):
 //   S^T = K Q^T : A = 16 keys x 32 dims of K, B = 32 dims x 16 columns of Q^T,
@@ -43,10 +44,11 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   constexpr int NW = 4;               // waves per workgroup
   constexpr int KL = KV ? MT * KS / 2 : MT * KS;  // 16-byte K loads per lane per chunk
 
-  __shared__ v4f sh_o[NW - 1][MD][64];
-  __shared__ float sh_m[NW - 1][64];
-  __shared__ float sh_l[NW - 1][64];
-  __shared__ int sh_bad[NW];
+  // Wave states at the end of a split, double-buffered by split parity.
+  __shared__ v4f sh_o[2][NW - 1][MD][64];
+  __shared__ float sh_m[2][NW - 1][64];
+  __shared__ float sh_l[2][NW - 1][64];
+  __shared__ int sh_bad[2][NW];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: SGPR arithmetic
@@ -57,7 +59,8 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   const int item = blockIdx.x / A.col_tiles;
   const int si = find_stream<0>(A.s, A.n_streams, item);
   const StreamArg& S = A.s[si];
-  const int split = item - S.block_begin;
+  const int split0 = (item - S.block_begin) * A.splits_per_wg;  // first split of the workgroup
+  const int n_sub = min(A.splits_per_wg, S.n_splits - split0);
   const int G = A.group;
   if (16 * ct >= G * S.n_rows) return;  // tile holds no column of this stream
 
@@ -84,22 +87,30 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
     }
   }
 
-  const int k_lo = split * A.split_keys;
-  const int k_hi = min(k_lo + A.split_keys, S.n_keys);
+  const int k_lo = split0 * A.split_keys;
+  const int k_hi = min(k_lo + n_sub * A.split_keys, S.n_keys);
   const int p_lo = k_lo / kPage;
   const int p_hi = (k_hi + kPage - 1) / kPage;
-  // The waves walk the split's pages in the order p_lo + wave, + NW, ...,
-  // read through a rotation by the split index: physical page
-  // p_lo + (p - p_lo + split) mod (pages of the split).  Contiguous slabs
-  // put the splits of a stream at regular strides, and without it every
-  // workgroup would touch the same offsets of its split at the same time.
-  // The rotation depends on the split alone, never on the batch.
-  const int np = p_hi - p_lo;
-  const int rot = np > 0 ? split % np : 0;
+  // Pages of a whole split.  With more than one split per workgroup the host
+  // makes it a multiple of NW, so wave w meets the same pages of every split
+  // (those p_lo(split) + w + NW i) as it would alone.
+  const int pps = A.split_keys / kPage;
+  // The split (0 .. n_sub-1) of the workgroup a page belongs to.
+  auto sub = [&](int p) { return (p - p_lo) / pps; };
+  // The waves walk a split's pages in the order p_lo(split) + wave, + NW,
+  // ..., read through a rotation by the split index: physical page
+  // p_lo(split) + (p - p_lo(split) + split) mod (pages of the split).
+  // Contiguous slabs put the splits of a stream at regular strides, and
+  // without it every workgroup would touch the same offsets of its split at
+  // the same time.  The rotation depends on the split alone, never on the
+  // batch.
   auto phys = [&](int p) {
-    int v = p - p_lo + rot;
+    const int sb = sub(p);
+    const int base = p_lo + sb * pps;
+    const int np = min(pps, p_hi - base);
+    int v = p - base + (split0 + sb) % np;
     if (v >= np) v -= np;
-    return p_lo + v;
+    return base + v;
   };
 
   v4f o[MD];
@@ -237,6 +248,63 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
       c0 = 0;
     }
   };
+  // The end of split `done` of the workgroup: the waves' states go to the
+  // LDS set of its parity and, after a barrier, wave 0 merges them in fixed
+  // wave order and writes the partial; every wave then starts the next split
+  // afresh.  The barrier only orders LDS: loads of the next split already in
+  // flight stay in flight.  Wave 0 reads a set before it reaches the next
+  // barrier, so the set is free again when the split after next ends.
+  int done = 0;
+  auto boundary = [&]() {
+    const int sp = done & 1;
+    // Per-column row sum across the four lane groups, in a fixed order.
+    float l_sum = rows4_sum(l_run);
+    if (wave > 0) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md) sh_o[sp][wave - 1][md][lane] = o[md];
+      sh_m[sp][wave - 1][lane] = m_run;
+      sh_l[sp][wave - 1][lane] = l_sum;
+    }
+    if (lane == 0) sh_bad[sp][wave] = bad ? 1 : 0;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wave == 0) {
+      bool any_bad = false;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) any_bad |= sh_bad[sp][w] != 0;
+      // Merge waves 1..NW-1 into wave 0 in fixed order.
+      float m_acc = m_run;
+      for (int w = 1; w < NW; ++w) {
+        const float mw = sh_m[sp][w - 1][lane];
+        const float lw = sh_l[sp][w - 1][lane];
+        const float M = fmaxf(m_acc, mw);
+        if (M == -INFINITY) continue;
+        const float a0 = __builtin_amdgcn_exp2f(m_acc - M);
+        const float aw = __builtin_amdgcn_exp2f(mw - M);
+#pragma unroll
+        for (int md = 0; md < MD; ++md) o[md] = o[md] * a0 + sh_o[sp][w - 1][md][lane] * aw;
+        l_sum = l_sum * a0 + lw * aw;
+        m_acc = M;
+      }
+      if (col_ok) {
+        const int64_t slot =
+            S.slot_base + ((int64_t)r * A.n_q_heads + h) * S.n_splits + split0 + done;
+        if (a == 0) {
+          A.ws_ml[2 * slot] = any_bad ? __builtin_nanf("") : m_acc;
+          A.ws_ml[2 * slot + 1] = l_sum;
+        }
+        float* dst = A.ws_o + slot * D + 4 * a;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) *reinterpret_cast<v4f*>(dst + 16 * md) = o[md];
+      }
+    }
+#pragma unroll
+    for (int md = 0; md < MD; ++md) o[md] = v4f{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    bad = false;
+    ++done;
+  };
+
   // Chunks i (p0, c0), i+1 (p1, c1) and i+2 (p2, c2), with their page tiles;
   // the page table is read once per page as a chunk first enters the queue.
   v4u krA[KL], vrA[MD], krB[KL], vrB[MD];
@@ -277,6 +345,9 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
     p1 = p2;
     c1 = c2;
     T1 = T2;
+    // the splits this wave has finished (its next chunk lies beyond them)
+    const int s_next = p0 < p_hi ? sub(p0) : n_sub;
+    while (done < s_next) boundary();
   };
   while (p0 < p_hi) {
     run_chunk(krA, vrA);
@@ -284,44 +355,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
     run_chunk(krB, vrB);
   }
 
-  // Per-column row sum across the four lane groups, in a fixed order.
-  l_run = rows4_sum(l_run);
-
-  if (wave > 0) {
-#pragma unroll
-    for (int md = 0; md < MD; ++md) sh_o[wave - 1][md][lane] = o[md];
-    sh_m[wave - 1][lane] = m_run;
-    sh_l[wave - 1][lane] = l_run;
-  }
-  if (lane == 0) sh_bad[wave] = bad ? 1 : 0;
-  __syncthreads();
-  if (wave != 0) return;
-
-  bool any_bad = false;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) any_bad |= sh_bad[w] != 0;
-  // Merge waves 1..NW-1 into wave 0 in fixed order.
-  for (int w = 1; w < NW; ++w) {
-    const float mw = sh_m[w - 1][lane];
-    const float lw = sh_l[w - 1][lane];
-    const float M = fmaxf(m_run, mw);
-    if (M == -INFINITY) continue;
-    const float a0 = __builtin_amdgcn_exp2f(m_run - M);
-    const float aw = __builtin_amdgcn_exp2f(mw - M);
-#pragma unroll
-    for (int md = 0; md < MD; ++md) o[md] = o[md] * a0 + sh_o[w - 1][md][lane] * aw;
-    l_run = l_run * a0 + lw * aw;
-    m_run = M;
-  }
-  if (!col_ok) return;
-  const int64_t slot = S.slot_base + ((int64_t)r * A.n_q_heads + h) * S.n_splits + split;
-  if (a == 0) {
-    A.ws_ml[2 * slot] = any_bad ? __builtin_nanf("") : m_run;
-    A.ws_ml[2 * slot + 1] = l_run;
-  }
-  float* dst = A.ws_o + slot * D + 4 * a;
-#pragma unroll
-  for (int md = 0; md < MD; ++md) *reinterpret_cast<v4f*>(dst + 16 * md) = o[md];
+  while (done < n_sub) boundary();
 }
 
 // out[row][h] = v_scale * sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j, in
@@ -405,7 +439,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs A) {
 
 template <int KV, int D>
 static int launch_partials_t(const DecodeArgs& A, int n_kv_heads, hipStream_t st) {
-  dim3 grid((unsigned)(A.total_splits * A.col_tiles), (unsigned)n_kv_heads);
+  dim3 grid((unsigned)(A.total_items * A.col_tiles), (unsigned)n_kv_heads);
   hipLaunchKernelGGL((decode_partial_kernel<KV, D>), grid, dim3(256), 0, st, A);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }

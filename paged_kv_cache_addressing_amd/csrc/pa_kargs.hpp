@@ -44,7 +44,7 @@ struct StreamArg {
   int32_t first_pos;    // absolute position of the first row
   int32_t n_keys;       // first_pos + n_rows: keys the last row sees
   int32_t n_splits;     // decode: ceil(n_keys / split_keys)
-  int32_t block_begin;  // decode: first split of the stream in the launch; prefill: first row tile
+  int32_t block_begin;  // decode: first workgroup item of the stream in the launch; prefill: first row tile
   int32_t row_begin;    // first row of the stream in the launch's row numbering
   int32_t full_begin;   // row-tile split mode: first of the stream's whole-split items
   int32_t part_begin;   // row-tile split mode: rank of its short last split's items, or -1
@@ -72,10 +72,10 @@ struct DecodeArgs {
   int32_t group;        // q heads per kv head
   int32_t split_keys;
   int32_t n_streams;
-  int32_t total_splits;
+  int32_t total_items;  // workgroup items: runs of splits_per_wg consecutive splits of a stream
   int32_t col_tiles;    // 16-column MFMA tiles per (split, kv head)
   int32_t total_rows;   // rows in this launch (merge grid)
-  int32_t pad0;
+  int32_t splits_per_wg;  // consecutive splits one workgroup computes
   float scale_log2;     // sm_scale * k_scale * log2(e)
   float v_scale;
   StreamArg s[kMaxLaunchStreams];

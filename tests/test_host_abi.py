@@ -222,7 +222,10 @@ def test_decode_plan_decode_batch_shape():
     splits, plan = _plan(ss)
     assert list(splits) == [16] * 8
     assert plan.total_splits == 128 and plan.col_tiles == 1
-    assert plan.partial_blocks == 512 and plan.merge_blocks == 8 * 24
+    # 512 one-split workgroups would take two rounds of the 256 CUs, so each
+    # workgroup computes two consecutive splits of its stream
+    assert plan.narrow_splits_per_wg == 2
+    assert plan.partial_blocks == 256 and plan.merge_blocks == 8 * 24
     slots = 8 * 24 * 16
     want = math.ceil(slots * 256 * 4 / 256) * 256 + math.ceil(slots * 2 * 4 / 256) * 256
     assert plan.workspace_bytes == want == pa.paged_attn_decode_workspace_size(ss, 24, 256)
@@ -240,6 +243,7 @@ def test_decode_plan_verify_rows_and_ragged_lengths():
     # per (split, kv head) covers them all; the streaming kernel runs none
     assert plan.col_tiles == 0
     assert plan.partial_blocks == plan.wide_blocks == sum(splits) * 4
+    assert plan.narrow_splits_per_wg == 0
 
 
 def test_decode_plan_kernel_choice_per_stream():
@@ -252,6 +256,7 @@ def test_decode_plan_kernel_choice_per_stream():
     assert plan.col_tiles == 2  # 30 columns
     assert plan.wide_blocks == 2 * 4
     assert plan.partial_blocks == 2 * 2 * 4 + 2 * 4
+    assert plan.narrow_splits_per_wg == 1  # one round of workgroups: no grouping
     # head_dim 128: 48 columns a wave, 192 a workgroup; a group of 16 with
     # 16 rows (256 columns) needs two row tiles of 12 rows
     ss = [stream(ctx_len=4096, n_rows=16, first_pos=4080)]
