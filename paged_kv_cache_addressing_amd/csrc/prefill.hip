@@ -106,8 +106,12 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   constexpr int NTH = 64 * NW;          // threads per workgroup
   constexpr int KF = MT * KS;           // K fragments (1 KiB) per step
   constexpr int VF = MD;                // V fragments per step
-  constexpr int KPW = KF / NW;          // DMA fragments per wave per step
-  constexpr int VPW = VF / NW;
+  // bf16 with wave pairs: only the consumer waves (P.V, no softmax) issue
+  // and await the K/V DMAs, so the producers' S/softmax phase carries none.
+  constexpr bool CLOAD = KV == 0 && PAIR;
+  constexpr int NLB = CLOAD ? NG : NW;  // bf16 loader waves
+  constexpr int KPW = KF / NLB;         // DMA fragments per loader wave per step
+  constexpr int VPW = VF / NLB;
   // K and V slot rings (see the step schedule): bf16 DMAs K three and V two
   // steps ahead; fp8 converts K(v+2) and V(v+1) into their slots in step v.
   constexpr int NSLOT = KV ? 2 : 3;     // K slots
@@ -294,7 +298,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   // S^T row m of m-tile mt holds key 8*(m/4) + 4*mt + m%4 of the step.
   const int krow = 8 * (n >> 2) + (n & 3);
 
-  // bf16 loaders: each wave DMAs KPW K fragments and VPW V fragments.
+  // bf16 loaders: loader wave lb DMAs KPW K fragments and VPW V fragments.
+  const bool bl = !CLOAD || !producer;
+  const int lb = CLOAD ? cg : wave;
   // Each DMA is the step's base in the page tile (o*D*2 bytes for both K
   // and V: wave-uniform, SGPRs) plus a per-lane offset that does not depend
   // on the step (loop invariant, hoisted into VGPRs).
@@ -302,10 +308,10 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
     const PageTile& T = page_k(v);
     const auto rs = tile_rsrc(T.k, kPage * D * 2);
     const int soff = (v & 7) * BK * D * 2;
-    v4u* dst = Kbase + sl * KSLOT + wave * KPW * 64;
+    v4u* dst = Kbase + sl * KSLOT + lb * KPW * 64;
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
-      const int f = wave * KPW + i, mt = f / KS, ks = f % KS;
+      const int f = lb * KPW + i, mt = f / KS, ks = f % KS;
       const int off = ((krow + 4 * mt) * D + 32 * ks + 8 * a) * 2;
       dma16(rs, off, soff, dst + i * 64);
     }
@@ -314,10 +320,10 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
     const PageTile& T = page_v(v);
     const auto rs = tile_rsrc(T.v, kPage * D * 2);
     const int soff = (v & 7) * BK * D * 2;
-    v4u* dst = Vbase + sl * VSLOT + wave * VPW * 64;
+    v4u* dst = Vbase + sl * VSLOT + lb * VPW * 64;
 #pragma unroll
     for (int i = 0; i < VPW; ++i) {
-      const int off = v_off<D, ESZ>(8 * a, 16 * (wave * VPW + i) + n) * 2;
+      const int off = v_off<D, ESZ>(8 * a, 16 * (lb * VPW + i) + n) * 2;
       dma16(rs, off, soff, dst + i * 64);
     }
   };
@@ -587,8 +593,14 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
     const int r0 = ph % 3, r1 = (ph + 1) % 3;  // staging of v+3, v+4
     int issued = 0;
     if (KV == 0) {
-      if (FAST || v + 2 < v_hi) { dma_v(v + 2, vslot(v + 2)); issued = 1; }
-      if (FAST || v + 3 < v_hi) { dma_k(v + 3, kslot(v + 3)); issued = 2; }
+      if (FAST || v + 2 < v_hi) {
+        if (bl) dma_v(v + 2, vslot(v + 2));
+        issued = 1;
+      }
+      if (FAST || v + 3 < v_hi) {
+        if (bl) dma_k(v + 3, kslot(v + 3));
+        issued = 2;
+      }
     } else {
       auto load = [&](auto nl) __attribute__((always_inline)) {
         constexpr int NL = decltype(nl)::value;
@@ -761,11 +773,13 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       const int n_st = v_hi - v_lo;
       v4f S0[MT][NT], S1[MT][NT];
       if (KV == 0) {
-        dma_k(v_lo, 0);
-        dma_v(v_lo, 0);
-        if (n_st > 1) dma_k(v_lo + 1, 1);
-        if (n_st > 1) dma_v(v_lo + 1, 1);
-        if (n_st > 2) dma_k(v_lo + 2, 2);
+        if (bl) {
+          dma_k(v_lo, 0);
+          dma_v(v_lo, 0);
+          if (n_st > 1) dma_k(v_lo + 1, 1);
+          if (n_st > 1) dma_v(v_lo + 1, 1);
+          if (n_st > 2) dma_k(v_lo + 2, 2);
+        }
         if (n_st > 2) wait_vmem<KPW + VPW>();
         else if (n_st > 1) wait_vmem<VPW>();
         else wait_vmem<0>();
