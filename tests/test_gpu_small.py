@@ -441,3 +441,88 @@ def test_chain_tree_gives_the_causal_bytes_and_trees_are_batch_invariant():
         torch.cuda.synchronize()
         r0, r1 = st.row_offset, st.row_offset + st.n_rows
         assert same_bytes(alone[r0:r1], both[r0:r1])
+
+
+# ----------------------------------------------------------------------------- guards and controls
+
+def _guarded(n_bytes: int, guard: int = 4096):
+    """A uint8 device buffer with `guard` canary bytes (0xA5) on each side of
+    an n_bytes window; returns (buffer, window)."""
+    buf = torch.full((n_bytes + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    return buf, buf[guard:guard + n_bytes]
+
+
+def _guards_intact(buf: torch.Tensor, n_bytes: int, guard: int = 4096) -> bool:
+    return bool((buf[:guard] == 0xA5).all()) and bool((buf[guard + n_bytes:] == 0xA5).all())
+
+
+def test_decode_split_groups_equal_alone_and_stay_in_their_buffers():
+    """512 one-split workgroups would take two rounds, so each workgroup
+    computes two consecutive 1,024-key splits; every stream alone (64
+    workgroups, one split each) gives the same bytes.  Workspace and output
+    sit between canary bytes that must survive."""
+    wl = workloads.build("groups", n_q_heads=24, n_kv_heads=4, head_dim=256, kv_dtype="bf16",
+                         ctx_lens=[16384] * 8, n_rows=[1] * 8, split_keys=1024, seed=91)
+    res = upload(wl)
+    _, plan = pa.paged_attn_decode_plan(res.streams, 24, 4, 256, 1024)
+    assert plan.narrow_splits_per_wg == 2
+    nb = pa.paged_attn_decode_workspace_size(res.streams, 24, 256, 1024)
+    wbuf, ws = _guarded(nb)
+    ob = res.q.numel() * 2
+    obuf, ow = _guarded(ob)
+    out = ow.view(torch.bfloat16).view(res.q.shape)
+    pa.paged_attn_decode(res.cache, res.streams, res.q, out=out, sm_scale=res.sm_scale,
+                         split_keys=1024, workspace=ws)
+    torch.cuda.synchronize()
+    assert _guards_intact(wbuf, nb) and _guards_intact(obuf, ob)
+    refs, sels = references(wl)
+    err = launch_error(wl, out, refs, sels)
+    say(f"split groups: normalised error {err:.3e}")
+    assert err <= tol(wl)
+    for st in res.streams:
+        alone = decode(res, streams=[st], split_keys=1024)
+        r0, r1 = st.row_offset, st.row_offset + st.n_rows
+        assert same_bytes(alone[r0:r1], out[r0:r1])
+
+
+def test_prefill_output_stays_in_its_buffer():
+    wl = workloads.build("pf-guard", n_q_heads=24, n_kv_heads=4, head_dim=256, kv_dtype="bf16",
+                         ctx_lens=[700, 1500], n_rows=[300, 77], seed=92)
+    res = upload(wl)
+    ob = res.q.numel() * 2
+    obuf, ow = _guarded(ob)
+    out = ow.view(torch.bfloat16).view(res.q.shape)
+    prefill(res, out=out)
+    assert _guards_intact(obuf, ob)
+    assert same_bytes(out, prefill(res))
+
+
+def test_fp8_swapped_scales_control_fails():
+    """V carries 8 times K's scale (V rows times 8 store the same codes); the
+    launch matches the oracle with the right scales and not with K's and V's
+    scales swapped."""
+    wl = workloads.build("scales", n_q_heads=24, n_kv_heads=4, head_dim=256, kv_dtype="fp8",
+                         ctx_lens=[3000, 5000], n_rows=[1, 16], seed=93)
+    wl.v_rows = [(v.float() * 8).to(torch.bfloat16) for v in wl.v_rows]
+    wl.v_scale = wl.v_scale * 8
+    res = upload(wl)
+    refs, sels = references(wl)
+    err = launch_error(wl, decode(res), refs, sels)
+    assert err <= tol(wl)
+    res.cache.k_scale, res.cache.v_scale = res.cache.v_scale, res.cache.k_scale
+    bad = launch_error(wl, decode(res), refs, sels)
+    say(f"scales: {err:.3e} right, {bad:.3e} swapped")
+    assert bad > tol(wl)
+
+
+def test_context_past_the_stored_rows_control_reads_poison():
+    """A descriptor that claims one position more than was stored makes its
+    row read the poisoned slot after the stream's last key: NaN."""
+    wl = workloads.build("ctx+1", n_q_heads=24, n_kv_heads=4, head_dim=256, kv_dtype="bf16",
+                         ctx_lens=[3000], n_rows=[1], seed=94)
+    res = upload(wl, poison_tail=True)
+    st = res.streams[0]
+    assert torch.isfinite(decode(res).float()).all()
+    over = pa.Stream(st.ctx_len + 1, 1, st.row_offset, st.first_pos + 1,
+                     page_table=st.page_table, layout=st.layout)
+    assert torch.isnan(decode(res, streams=[over]).float()).any()
