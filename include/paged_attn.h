@@ -239,6 +239,11 @@ PA_API int write_kv(const pa_kv_cache *cache, const pa_stream *streams, int32_t 
  * MFMA tile per workgroup; a wider one (verify rows) runs on the row-tile
  * kernel, one workgroup per (split, kv head) whose LDS K/V tiles serve every
  * row and q head of the group, so each split is read from HBM once.
+ * When the register-streaming workgroups of a call would take two or more
+ * rounds of the device's 256 compute units, one workgroup computes several
+ * consecutive splits of its stream (pa_decode_plan.narrow_splits_per_wg);
+ * every split is still computed as by a workgroup of its own, so no
+ * partial's bytes depend on that grouping.
  * n_rows per stream <= PA_DECODE_MAX_ROWS; sm_scale > 0 (1/sqrt(head_dim)
  * is the usual value); split_keys a positive multiple of 256.
  * The workspace (device, >= paged_attn_decode_workspace_size bytes, 256-byte
