@@ -456,16 +456,19 @@ def _guards_intact(buf: torch.Tensor, n_bytes: int, guard: int = 4096) -> bool:
     return bool((buf[:guard] == 0xA5).all()) and bool((buf[guard + n_bytes:] == 0xA5).all())
 
 
-def test_decode_split_groups_equal_alone_and_stay_in_their_buffers():
-    """512 one-split workgroups would take two rounds, so each workgroup
-    computes two consecutive 1,024-key splits; every stream alone (64
-    workgroups, one split each) gives the same bytes.  Workspace and output
-    sit between canary bytes that must survive."""
+@pytest.mark.parametrize("n_streams,spw", [(8, 2), (10, 3)])
+def test_decode_split_groups_equal_alone_and_stay_in_their_buffers(n_streams, spw):
+    """8 (10) streams of 16 splits make 512 (640) one-split workgroups, more
+    than two rounds, so each workgroup computes 2 (3) consecutive 1,024-key
+    splits (with 3, each stream's last workgroup has one split); every stream
+    alone (64 workgroups, one split each) gives the same bytes.  Workspace and
+    output sit between canary bytes that must survive."""
     wl = workloads.build("groups", n_q_heads=24, n_kv_heads=4, head_dim=256, kv_dtype="bf16",
-                         ctx_lens=[16384] * 8, n_rows=[1] * 8, split_keys=1024, seed=91)
+                         ctx_lens=[16384] * n_streams, n_rows=[1] * n_streams, split_keys=1024,
+                         seed=91)
     res = upload(wl)
     _, plan = pa.paged_attn_decode_plan(res.streams, 24, 4, 256, 1024)
-    assert plan.narrow_splits_per_wg == 2
+    assert plan.narrow_splits_per_wg == spw
     nb = pa.paged_attn_decode_workspace_size(res.streams, 24, 256, 1024)
     wbuf, ws = _guarded(nb)
     ob = res.q.numel() * 2
