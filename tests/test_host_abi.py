@@ -281,3 +281,24 @@ def test_decode_plan_groups_streams_beyond_one_launch():
     empty = [stream(ctx_len=512, first_pos=511, row_offset=0, n_rows=0)]
     _, plan = _plan(empty)
     assert plan.n_launch_groups == 0 and plan.workspace_bytes == 0
+
+
+def test_decode_plan_split_grouping_rule():
+    """Consecutive splits share a register-streaming workgroup only once the
+    one-split workgroups would take two or more rounds of 256 CUs, and only
+    when a split's pages divide over the four waves (split_keys % 1024 == 0);
+    the grouping is ceil(workgroups / 256)."""
+    def batch(n, ctx):
+        return [stream(ctx_len=ctx, first_pos=ctx - 1, row_offset=i) for i in range(n)]
+    # 4 streams x 16 splits x 4 kv heads = 256 workgroups: one round, no grouping
+    _, plan = _plan(batch(4, 65536))
+    assert plan.narrow_splits_per_wg == 1 and plan.partial_blocks == 256
+    # 12 streams: 768 one-split workgroups -> 3 splits each, 16 splits -> 6 per stream
+    _, plan = _plan(batch(12, 65536))
+    assert plan.narrow_splits_per_wg == 3 and plan.partial_blocks == 12 * 6 * 4
+    # 512-key splits (two pages, not a multiple of four): never grouped
+    _, plan = _plan(batch(8, 65536), split=512)
+    assert plan.narrow_splits_per_wg == 1 and plan.partial_blocks == 8 * 128 * 4
+    # 2,048-key splits: 8 x 32 x 4 = 1,024 workgroups -> 4 splits each
+    _, plan = _plan(batch(8, 65536), split=2048)
+    assert plan.narrow_splits_per_wg == 4 and plan.partial_blocks == 8 * 8 * 4
