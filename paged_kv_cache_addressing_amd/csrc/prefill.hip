@@ -11,9 +11,9 @@
 // Work split.  A workgroup owns one kv head, HW of its q heads and a tile of
 // query rows; its column groups own 16*NT MFMA columns each, a column being
 // one (row, q head) pair (column c of the workgroup is (c / HW, c % HW)).
-// bf16 at head_dim 256: 4 groups of two n-tiles, each a producer/consumer
-// wave pair on one SIMD; fp8 at 256: 8 waves of one n-tile (two per SIMD);
-// at 128: 4 waves of three.  The K/V tiles in LDS serve all HW heads, and
+// At head_dim 256: 4 column groups, each a producer/consumer wave pair on
+// one SIMD, of three n-tiles (prefill) or two (split mode); at 128: 4 waves
+// of three n-tiles, each running both phases.  The K/V tiles in LDS serve all HW heads, and
 // the other head groups of the same kv head run on the same XCD, so K/V
 // also hit in L2.
 //   S^T (32 keys x 16NT cols) = K Q^T    : 2 m-tiles x NT n-tiles x D/32 k-steps
@@ -38,7 +38,10 @@
 // converted to bf16 fragment order once, one step ahead.  In step v the
 // S product S(v+1) = K(v+1) Q^T runs on the matrix cores while the VALU does
 // the softmax of S(v); O += V(v) P(v) follows in the same wave, or (wave
-// pairs) in the consumer wave one step later.
+// pairs) in the consumer wave one step later.  With pairs, bf16 K/V DMAs are
+// issued and awaited by the consumer waves only; fp8 in split mode, when the
+// last column group holds no column, is loaded and converted by that idle
+// pair alone.
 //
 // Softmax.  Logits stay raw until exp2(fma(s, c, -m c)).  A row's running max
 // moves only when the new maximum exceeds it by more than 2^8 in probability
