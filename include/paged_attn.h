@@ -287,8 +287,10 @@ PA_API int paged_attn_decode_merge(const pa_kv_cache *cache, const pa_stream *st
 
 /* Launch plan of a decode call, for callers that size grids or check
  * scheduling: per stream its split count (splits_out, n_streams entries, may
- * be NULL), and the totals.  Host only; validates like paged_attn_decode
- * minus the device pointers. */
+ * be NULL), and the totals.  kv_dtype (pa_kv_dtype) selects the kernels the
+ * block counts refer to; split counts and workspace size do not depend on
+ * it.  Host only; validates like paged_attn_decode minus the device
+ * pointers. */
 typedef struct pa_decode_plan {
   int32_t n_launch_groups;   /* launch groups (streams are grouped, at most 32 a group) */
   int32_t total_splits;      /* sum over streams of their split counts */
@@ -303,7 +305,7 @@ typedef struct pa_decode_plan {
 
 PA_API int paged_attn_decode_plan(const pa_stream *streams, int32_t n_streams, int32_t n_q_heads,
                            int32_t n_kv_heads, int32_t head_dim, int32_t split_keys,
-                           int32_t *splits_out, pa_decode_plan *plan);
+                           int32_t kv_dtype, int32_t *splits_out, pa_decode_plan *plan);
 
 /* ----------------------------------------------------------------- prefill
  * Prompt-chunk prefill (pull request #1373, prompt rows; pull request #2011,

@@ -18,6 +18,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
+from . import validate as _v
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
 
@@ -114,8 +116,8 @@ def lib():
         L.paged_attn_decode_merge.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream), i32,
                                               P, i32, i32, P, sz, P]
         L.paged_attn_decode_plan.restype = C.c_int
-        L.paged_attn_decode_plan.argtypes = [C.POINTER(pa_stream), i32, i32, i32, i32, i32, P,
-                                             C.POINTER(pa_decode_plan)]
+        L.paged_attn_decode_plan.argtypes = [C.POINTER(pa_stream), i32, i32, i32, i32, i32, i32,
+                                             P, C.POINTER(pa_decode_plan)]
         L.paged_attn_prefill.restype = C.c_int
         L.paged_attn_prefill.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream), i32, P, P,
                                          i32, f32, P]
@@ -285,11 +287,19 @@ def _ids(ids):
     return np.ascontiguousarray(ids, np.int32)
 
 
+def _page_bytes(cache: KVCache) -> int:
+    ps = cache.page_stride or cache.n_kv_heads * PAGE_POSITIONS * cache.head_dim
+    return ps * (2 if cache.dtype == "bf16" else 1)
+
+
 def page_copy(cache: KVCache, src_ids, dst_ids, stream=None) -> None:
     """Device copy of whole pages src_ids[i] -> dst_ids[i] (K and V)."""
     s, d = _ids(src_ids), _ids(dst_ids)
     if len(s) != len(d):
         raise ValueError("src_ids and dst_ids differ in length")
+    dev = []
+    _v.cache(dev, cache, len(s) > 0)
+    _v.on_gpu(dev)
     cc = cache.c()
     _check(lib().page_copy(C.byref(cc), s.ctypes.data_as(C.c_void_p), d.ctypes.data_as(C.c_void_p),
                            len(s), _hip_stream(stream)), "page_copy")
@@ -298,6 +308,12 @@ def page_copy(cache: KVCache, src_ids, dst_ids, stream=None) -> None:
 def page_save(cache: KVCache, ids, host_k, host_v, stream=None) -> None:
     """Copy whole pages to host tensors (page ids[i] at row i of each)."""
     a = _ids(ids)
+    dev = []
+    _v.cache(dev, cache, len(a) > 0)
+    if len(a):
+        _v.host_pages("host_k", host_k, len(a) * _page_bytes(cache))
+        _v.host_pages("host_v", host_v, len(a) * _page_bytes(cache))
+    _v.on_gpu(dev)
     cc = cache.c()
     _check(lib().page_save(C.byref(cc), a.ctypes.data_as(C.c_void_p), len(a), _ptr(host_k),
                            _ptr(host_v), _hip_stream(stream)), "page_save")
@@ -306,6 +322,12 @@ def page_save(cache: KVCache, ids, host_k, host_v, stream=None) -> None:
 def page_restore(cache: KVCache, ids, host_k, host_v, stream=None) -> None:
     """Copy host tensors (row i -> page ids[i]) back into the pool."""
     a = _ids(ids)
+    dev = []
+    _v.cache(dev, cache, len(a) > 0)
+    if len(a):
+        _v.host_pages("host_k", host_k, len(a) * _page_bytes(cache))
+        _v.host_pages("host_v", host_v, len(a) * _page_bytes(cache))
+    _v.on_gpu(dev)
     cc = cache.c()
     _check(lib().page_restore(C.byref(cc), a.ctypes.data_as(C.c_void_p), len(a), _ptr(host_k),
                               _ptr(host_v), _hip_stream(stream)), "page_restore")
@@ -333,8 +355,28 @@ def page_pool_destroy(pool: PagePool) -> None:
 
 # ----------------------------------------------------------------------------- kernels
 
+def _keep_alive(stream, *tensors) -> None:
+    """Tensors allocated here on torch's current stream but used by kernels
+    enqueued on another stream: tell the caching allocator, so their memory
+    is not handed out again before that stream's work has finished."""
+    if stream is None:
+        return
+    import torch
+    if stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        t.record_stream(stream)
+
+
 def write_kv(cache: KVCache, streams, k_new, v_new, stream=None) -> None:
     """Store bf16 rows [rows][Hkv][D] at each stream's positions first_pos.."""
+    dev = []
+    _v.cache(dev, cache, _v.any_paged(streams))
+    rows = _v.streams(dev, cache, streams)
+    if rows:
+        _v.dense_rows(dev, "k_new", k_new, cache.n_kv_heads, cache.head_dim, rows)
+        _v.dense_rows(dev, "v_new", v_new, cache.n_kv_heads, cache.head_dim, rows)
+    _v.on_gpu(dev)
     arr, n = _streams(streams)
     cc = cache.c()
     _check(lib().write_kv(C.byref(cc), arr, n, _ptr(k_new), _ptr(v_new), _hip_stream(stream)),
@@ -349,36 +391,78 @@ def paged_attn_decode_workspace_size(streams, n_q_heads: int, head_dim: int,
 
 
 def paged_attn_decode_plan(streams, n_q_heads: int, n_kv_heads: int, head_dim: int,
-                           split_keys: int = DEFAULT_SPLIT_KEYS):
+                           split_keys: int = DEFAULT_SPLIT_KEYS, kv_dtype: str = "bf16"):
     """(per-stream split counts, pa_decode_plan) without launching anything."""
     arr, n = _streams(streams)
     splits = np.zeros(max(n, 1), np.int32)
     plan = pa_decode_plan()
     _check(lib().paged_attn_decode_plan(arr, n, int(n_q_heads), int(n_kv_heads), int(head_dim),
-                                        int(split_keys), splits.ctypes.data_as(C.c_void_p),
+                                        int(split_keys), _kv_code(kv_dtype),
+                                        splits.ctypes.data_as(C.c_void_p),
                                         C.byref(plan)), "paged_attn_decode_plan")
     return splits[:n], plan
 
 
+def _kv_code(kv_dtype: str) -> int:
+    if kv_dtype == "bf16":
+        return PA_KV_BF16
+    if kv_dtype == "fp8":
+        return PA_KV_FP8_E4M3
+    raise ValueError(f"unknown KV dtype {kv_dtype!r}")
+
+
+def _check_attention(dev: list, cache: KVCache, streams, q, out, max_rows=None) -> int:
+    """Validate the tensors of an attention call (device checks are appended
+    to `dev`, for _v.on_gpu once every other check has passed); returns
+    n_q_heads."""
+    if q is None and out is None:
+        raise ValueError("q or out is required")
+    ref = q if q is not None else out
+    _v.cache(dev, cache, _v.any_paged(streams))
+    rows = _v.streams(dev, cache, streams, max_rows)
+    if not hasattr(ref, "shape") or len(ref.shape) != 3:
+        raise ValueError("q / out must be [rows][n_q_heads][head_dim]")
+    n_q_heads = int(ref.shape[1])
+    if n_q_heads % cache.n_kv_heads:
+        raise ValueError(f"{n_q_heads} q heads is not a multiple of {cache.n_kv_heads} kv heads")
+    if q is not None:
+        _v.dense_rows(dev, "q", q, n_q_heads, cache.head_dim, rows)
+    if out is not None:
+        _v.dense_rows(dev, "out", out, n_q_heads, cache.head_dim, rows)
+    return n_q_heads
+
+
 def paged_attn_decode(cache: KVCache, streams, q, out=None, sm_scale: float | None = None,
                       split_keys: int = DEFAULT_SPLIT_KEYS, workspace=None, stream=None):
-    """Split-K decode; q/out bf16 [rows][Hq][D]. Returns out."""
+    """Split-K decode; q/out bf16 [rows][Hq][D]. Returns out.
+
+    A workspace or output allocated here on torch's current stream is marked
+    as used by `stream`, so it cannot be reused while the kernels run there."""
     import torch
-    n_q_heads = int(q.shape[1])
+    dev = []
+    n_q_heads = _check_attention(dev, cache, streams, q, out, DECODE_MAX_ROWS)
+    made = []
     if out is None:
         out = torch.empty_like(q)
+        made.append(out)
     if sm_scale is None:
         sm_scale = cache.head_dim ** -0.5
     arr, n = _streams(streams)
+    need = int(lib().paged_attn_decode_workspace_size(arr, n, n_q_heads, cache.head_dim,
+                                                      int(split_keys)))
     if workspace is None:
-        nb = int(lib().paged_attn_decode_workspace_size(arr, n, n_q_heads, cache.head_dim,
-                                                        int(split_keys)))
-        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+        _v.on_gpu(dev)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        made.append(workspace)
+    else:
+        _v.workspace(dev, workspace, need)
+        _v.on_gpu(dev)
     cc = cache.c()
     _check(lib().paged_attn_decode(C.byref(cc), arr, n, _ptr(q), _ptr(out), n_q_heads,
                                    float(sm_scale), int(split_keys), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(),
                                    _hip_stream(stream)), "paged_attn_decode")
+    _keep_alive(stream, *made)
     return out
 
 
@@ -394,11 +478,16 @@ def paged_attn_decode_partials(cache: KVCache, streams, q, workspace,
                                sm_scale: float | None = None,
                                split_keys: int = DEFAULT_SPLIT_KEYS, stream=None) -> None:
     """Split partials (m, l, o) of every (row, head, split) into workspace."""
+    dev = []
+    n_q_heads = _check_attention(dev, cache, streams, q, None, DECODE_MAX_ROWS)
     if sm_scale is None:
         sm_scale = cache.head_dim ** -0.5
     arr, n = _streams(streams)
+    _v.workspace(dev, workspace, int(lib().paged_attn_decode_workspace_size(
+        arr, n, n_q_heads, cache.head_dim, int(split_keys))))
+    _v.on_gpu(dev)
     cc = cache.c()
-    _check(lib().paged_attn_decode_partials(C.byref(cc), arr, n, _ptr(q), int(q.shape[1]),
+    _check(lib().paged_attn_decode_partials(C.byref(cc), arr, n, _ptr(q), n_q_heads,
                                             float(sm_scale), int(split_keys), _ptr(workspace),
                                             workspace.numel() * workspace.element_size(),
                                             _hip_stream(stream)), "paged_attn_decode_partials")
@@ -407,9 +496,14 @@ def paged_attn_decode_partials(cache: KVCache, streams, q, workspace,
 def paged_attn_decode_merge(cache: KVCache, streams, out, workspace,
                             split_keys: int = DEFAULT_SPLIT_KEYS, stream=None):
     """Fixed-order LSE merge of the workspace partials into out (bf16)."""
+    dev = []
+    n_q_heads = _check_attention(dev, cache, streams, None, out, DECODE_MAX_ROWS)
     arr, n = _streams(streams)
+    _v.workspace(dev, workspace, int(lib().paged_attn_decode_workspace_size(
+        arr, n, n_q_heads, cache.head_dim, int(split_keys))))
+    _v.on_gpu(dev)
     cc = cache.c()
-    _check(lib().paged_attn_decode_merge(C.byref(cc), arr, n, _ptr(out), int(out.shape[1]),
+    _check(lib().paged_attn_decode_merge(C.byref(cc), arr, n, _ptr(out), n_q_heads,
                                          int(split_keys), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(),
                                          _hip_stream(stream)), "paged_attn_decode_merge")
@@ -420,12 +514,18 @@ def paged_attn_prefill(cache: KVCache, streams, q, out=None, sm_scale: float | N
                        stream=None):
     """Causal prefill of every row of every stream; q/out bf16 [rows][Hq][D]."""
     import torch
+    dev = []
+    n_q_heads = _check_attention(dev, cache, streams, q, out)
+    _v.on_gpu(dev)
+    made = []
     if out is None:
         out = torch.empty_like(q)
+        made.append(out)
     if sm_scale is None:
         sm_scale = cache.head_dim ** -0.5
     arr, n = _streams(streams)
     cc = cache.c()
-    _check(lib().paged_attn_prefill(C.byref(cc), arr, n, _ptr(q), _ptr(out), int(q.shape[1]),
+    _check(lib().paged_attn_prefill(C.byref(cc), arr, n, _ptr(q), _ptr(out), n_q_heads,
                                     float(sm_scale), _hip_stream(stream)), "paged_attn_prefill")
+    _keep_alive(stream, *made)
     return out

@@ -465,7 +465,8 @@ size_t paged_attn_decode_workspace_size(const pa_stream* streams, int32_t n_stre
 
 int paged_attn_decode_plan(const pa_stream* streams, int32_t n_streams, int32_t n_q_heads,
                            int32_t n_kv_heads, int32_t head_dim, int32_t split_keys,
-                           int32_t* splits_out, pa_decode_plan* plan) {
+                           int32_t kv_dtype, int32_t* splits_out, pa_decode_plan* plan) {
+  if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3) return PA_EINVAL;
   int rc = check_streams_shape(streams, n_streams, n_q_heads, n_kv_heads, head_dim,
                                PA_DECODE_MAX_ROWS);
   if (rc != PA_OK) return rc;
@@ -477,8 +478,7 @@ int paged_attn_decode_plan(const pa_stream* streams, int32_t n_streams, int32_t 
   if (plan) {
     std::memset(plan, 0, sizeof *plan);
     const int32_t group = n_q_heads / n_kv_heads;
-    // (a workgroup's column count does not depend on the KV dtype)
-    const RowTiling W = wide_tiling(PA_KV_BF16, head_dim, group);
+    const RowTiling W = wide_tiling(kv_dtype, head_dim, group);
     plan->n_launch_groups = (int32_t)P.groups.size();
     for (const auto& grp : P.groups) {
       int32_t tr = 0, narrow_splits = 0, wide_items = 0;

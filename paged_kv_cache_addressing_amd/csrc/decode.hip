@@ -104,10 +104,12 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   // without it every workgroup would touch the same offsets of its split at
   // the same time.  The rotation depends on the split alone, never on the
   // batch.
+  // A look-ahead may ask for a page at or past p_hi (its result is never
+  // used); np is kept >= 1 there so the remainder stays defined.
   auto phys = [&](int p) {
     const int sb = sub(p);
     const int base = p_lo + sb * pps;
-    const int np = min(pps, p_hi - base);
+    const int np = max(1, min(pps, p_hi - base));
     int v = p - base + (split0 + sb) % np;
     if (v >= np) v -= np;
     return base + v;
