@@ -8,9 +8,11 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_cache_addressing_amd as pa
 import workloads
 from tests._gpu import decode, launch_error, references, same_bytes, say
+from tests._util import bits16
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +86,16 @@ def test_shared_prefix_with_copy_on_write_last_page():
     out_s = pa.paged_attn_decode(solo, [pa.Stream(ctx_b, 1, 1, ctx_b - 1, page_table=pt_s)], q)
     torch.cuda.synchronize()
     assert same_bytes(out_b[1], out_s[1])
+    # and B's row against the oracle over its logical context (A's prefix rows
+    # followed by B's own)
+    kc = np.zeros((ctx_b, HKV, D), np.uint16)
+    vc = np.zeros_like(kc)
+    oracle.store(kc, vc, oracle.DTYPE_BF16, bits16(k), bits16(v), 0)
+    ref = oracle.attention(kc, vc, oracle.DTYPE_BF16, bits16(q[1:2].cpu()), ctx_b - 1, HKV, ctx_b,
+                           sm_scale=D ** -0.5)
+    err = oracle.normalised_error(out_b[1:2].float().cpu().numpy(), ref)
+    say(f"shared prefix: stream B error {err:.3e}")
+    assert err <= 1e-2
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
