@@ -285,6 +285,25 @@ PA_API int paged_attn_decode_merge(const pa_kv_cache *cache, const pa_stream *st
                                    int32_t split_keys, const void *workspace,
                                    size_t workspace_bytes, void *hip_stream);
 
+/* paged_attn_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The partials live in a fixed
+ * device array of PA_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends; the call allocates and frees
+ * nothing.  Same validation, arguments and output bytes as
+ * paged_attn_decode; PA_EWORKSPACE when the call's partials
+ * (paged_attn_decode_workspace_size) exceed the array.  All calls on one
+ * GPU share that array: calls that overlap on one GPU (from several host
+ * threads, or on several HIP streams at once) race and must be serialised by
+ * the caller.  The first call on a device looks the array's address up
+ * (PA_EDEVICE if that fails). */
+#define PA_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+PA_API int paged_attn_decode_noalloc(const pa_kv_cache *cache, const pa_stream *streams,
+                                     int32_t n_streams, const void *q, void *out,
+                                     int32_t n_q_heads, float sm_scale, int32_t split_keys,
+                                     void *hip_stream);
+
 /* Launch plan of a decode call, for callers that size grids or check
  * scheduling: per stream its split count (splits_out, n_streams entries, may
  * be NULL), and the totals.  kv_dtype (pa_kv_dtype) selects the kernels the

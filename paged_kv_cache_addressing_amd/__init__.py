@@ -27,6 +27,7 @@ PAGE_POSITIONS = 256
 DEFAULT_SPLIT_KEYS = 4096
 DECODE_MAX_ROWS = 16
 TREE_MAX_ROWS = 32  # rows of a stream that carries an ancestor table
+NOALLOC_SCRATCH_BYTES = 128 << 20  # the fixed scratch of paged_attn_decode_noalloc
 
 PA_OK, PA_EINVAL, PA_ERANGE, PA_ENOSPC, PA_ETOOBIG, PA_EWORKSPACE, PA_EDEVICE, PA_EUNSUPPORTED = (
     0, -1, -2, -3, -4, -5, -6, -7)
@@ -37,7 +38,8 @@ EXPORTS = ["pa_status_string", "pa_version", "page_pool_create", "page_pool_dest
            "page_pool_alloc", "page_pool_free", "page_pool_free_count", "page_pool_share",
            "page_pool_refcount", "page_copy", "page_save", "page_restore", "write_kv",
            "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_partials",
-           "paged_attn_decode_merge", "paged_attn_decode_plan", "paged_attn_prefill"]
+           "paged_attn_decode_merge", "paged_attn_decode_plan", "paged_attn_prefill",
+           "paged_attn_decode_noalloc"]
 
 
 class PagedAttnError(RuntimeError):
@@ -118,6 +120,9 @@ def lib():
         L.paged_attn_decode_plan.restype = C.c_int
         L.paged_attn_decode_plan.argtypes = [C.POINTER(pa_stream), i32, i32, i32, i32, i32, i32,
                                              P, C.POINTER(pa_decode_plan)]
+        L.paged_attn_decode_noalloc.restype = C.c_int
+        L.paged_attn_decode_noalloc.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream),
+                                                i32, P, P, i32, f32, i32, P]
         L.paged_attn_prefill.restype = C.c_int
         L.paged_attn_prefill.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream), i32, P, P,
                                          i32, f32, P]
@@ -463,6 +468,24 @@ def paged_attn_decode(cache: KVCache, streams, q, out=None, sm_scale: float | No
                                    workspace.numel() * workspace.element_size(),
                                    _hip_stream(stream)), "paged_attn_decode")
     _keep_alive(stream, *made)
+    return out
+
+
+def paged_attn_decode_noalloc(cache: KVCache, streams, q, out, sm_scale: float | None = None,
+                              split_keys: int = DEFAULT_SPLIT_KEYS, stream=None):
+    """Split-K decode with the partials in the library's fixed device scratch
+    (no device allocation anywhere, so out must be given).  Calls that
+    overlap on one GPU race on that scratch."""
+    dev = []
+    n_q_heads = _check_attention(dev, cache, streams, q, out, DECODE_MAX_ROWS)
+    _v.on_gpu(dev)
+    if sm_scale is None:
+        sm_scale = cache.head_dim ** -0.5
+    arr, n = _streams(streams)
+    cc = cache.c()
+    _check(lib().paged_attn_decode_noalloc(C.byref(cc), arr, n, _ptr(q), _ptr(out), n_q_heads,
+                                           float(sm_scale), int(split_keys),
+                                           _hip_stream(stream)), "paged_attn_decode_noalloc")
     return out
 
 

@@ -695,6 +695,25 @@ int paged_attn_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_
   return PA_OK;
 }
 
+int paged_attn_decode_noalloc(const pa_kv_cache* cache, const pa_stream* streams,
+                              int32_t n_streams, const void* q, void* out, int32_t n_q_heads,
+                              float sm_scale, int32_t split_keys, void* hip_stream) {
+  static_assert(pa::kNoAllocScratchBytes == (size_t)PA_NOALLOC_SCRATCH_BYTES,
+                "header and library agree on the scratch size");
+  int rc = check_call(cache, streams, n_streams, n_q_heads, PA_DECODE_MAX_ROWS);
+  if (rc != PA_OK) return rc;
+  DecodePlan P;
+  rc = plan_decode(streams, n_streams, n_q_heads, split_keys, P);
+  if (rc != PA_OK) return rc;
+  if (P.groups.empty()) return PA_OK;
+  if (ws_bytes(P.total_slots, cache->head_dim) > pa::kNoAllocScratchBytes) return PA_EWORKSPACE;
+  void* scratch = nullptr;
+  rc = pa::noalloc_scratch(&scratch);
+  if (rc != 0) return rc;
+  return paged_attn_decode(cache, streams, n_streams, q, out, n_q_heads, sm_scale, split_keys,
+                           scratch, pa::kNoAllocScratchBytes, hip_stream);
+}
+
 int paged_attn_prefill(const pa_kv_cache* cache, const pa_stream* streams, int32_t n_streams,
                        const void* q, void* out, int32_t n_q_heads, float sm_scale,
                        void* hip_stream) {

@@ -23,4 +23,10 @@ int launch_prefill(const PrefillArgs& A, int kv_dtype, int head_dim, hipStream_t
 int launch_write_kv(const WriteArgs& A, int kv_dtype, int head_dim, hipStream_t st);
 int launch_page_copy(const PageCopyArgs& A, hipStream_t st);
 
+// Bytes of the fixed device scratch behind paged_attn_decode_noalloc.
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+// Device address of the current device's scratch (looked up once per
+// device); returns 0, or -6 if the lookup failed.
+int noalloc_scratch(void** ptr);
+
 }  // namespace pa
