@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpaged_attn.so")
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "write_kv.hip", "pages.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "write_kv.hip", "pages.hip", "noalloc.hip",
+           "verify.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

@@ -172,7 +172,8 @@ RowTiling prefill_tiling(int32_t kv_dtype, int32_t head_dim, int32_t group) {
 // fits the workgroup's columns (the whole group whenever it fits), so every
 // split's K/V is read by as few workgroups as possible.
 RowTiling wide_tiling(int32_t kv_dtype, int32_t head_dim, int32_t group) {
-  const int32_t cols = pa::prefill_wg_columns(kv_dtype, head_dim, true);
+  const int32_t cols = kv_dtype == PA_KV_FP8_E4M3 ? pa::verify_wg_columns(head_dim)
+                                                  : pa::prefill_wg_columns(kv_dtype, head_dim, true);
   int32_t hw = 1;
   for (int32_t d = 1; d <= group && d <= cols; ++d)
     if (group % d == 0) hw = d;
@@ -639,7 +640,9 @@ int launch_partials(const DecodeLaunch& D, const pa_kv_cache* cache, hipStream_t
     if (rc != 0) return rc;
   }
   if (D.wide.n_streams > 0) {
-    const int rc = pa::launch_prefill(D.wide, cache->dtype, cache->head_dim, st);
+    const int rc = cache->dtype == PA_KV_FP8_E4M3
+                       ? pa::launch_verify(D.wide, cache->head_dim, st)
+                       : pa::launch_prefill(D.wide, cache->dtype, cache->head_dim, st);
     if (rc != 0) return rc;
   }
   return 0;

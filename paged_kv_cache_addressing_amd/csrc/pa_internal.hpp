@@ -20,6 +20,10 @@ int prefill_columns(int kv_dtype, int head_dim, bool split);
 // MFMA columns one row-tile workgroup covers (all its column groups).
 int prefill_wg_columns(int kv_dtype, int head_dim, bool split);
 int launch_prefill(const PrefillArgs& A, int kv_dtype, int head_dim, hipStream_t st);
+// fp8 verify kernel: split-K partials of decode streams with many columns
+// (PrefillArgs in split mode, fp8 KV).
+int verify_wg_columns(int head_dim);
+int launch_verify(const PrefillArgs& A, int head_dim, hipStream_t st);
 int launch_write_kv(const WriteArgs& A, int kv_dtype, int head_dim, hipStream_t st);
 int launch_page_copy(const PageCopyArgs& A, hipStream_t st);
 

@@ -37,6 +37,11 @@ static_assert(prefill_groups(0, 256) * prefill_ntiles(0, 256, true) ==
                   prefill_groups(1, 128) * prefill_ntiles(1, 128, true),
               "workgroup columns independent of the KV dtype");
 
+// fp8 verify kernel (wide decode streams with fp8 KV): 16-column n-tiles per
+// wave; its eight waves hold two column halves, so a workgroup covers
+// 32 * verify_ntiles columns (96 at head_dim 256, 128 at 128).
+constexpr int verify_ntiles(int head_dim) { return head_dim >= 256 ? 3 : 4; }
+
 struct StreamArg {
   int32_t layout;       // 0 paged, 1 slab
   int32_t n_rows;       // query rows of the stream in this call

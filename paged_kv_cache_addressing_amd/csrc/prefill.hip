@@ -61,37 +61,6 @@
 
 namespace pa {
 
-// Wait until at most N of this wave's vector-memory loads are outstanding
-// (LDS-DMA loads included; they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier for LDS hand-off only: this wave's LDS operations are
-// complete, then s_barrier.  Unlike __syncthreads() it does not wait for
-// outstanding vector-memory loads, so LDS-DMA prefetches stay in flight
-// across it (their completion is awaited explicitly with vmcnt).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// LDS-DMA through a buffer resource spanning one page tile: each lane's 16
-// bytes at voff + soff land at lds_dst + 16 * lane.  The buffer form is used
-// rather than the global one because the compiler counts a global LDS-DMA as
-// a flat access that may retire out of order with LDS reads; while one is in
-// flight it then waits for every LDS read with lgkmcnt(0), which undoes the
-// fragment read-ahead.  Offsets past the tile read zeros.
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
-  // dword 3: 32-bit data format (required for untyped access), no swizzle
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, int voff, int soff, v4u* lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
-}
-
 template <int KV, int D, bool SPLIT>
 __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const PrefillArgs A) {
   // A workgroup owns one kv head g, HW = heads_per_wg of its q heads (head
@@ -147,7 +116,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
   constexpr bool split_mode = SPLIT;  // the host launches this instance iff split_keys > 0
 
   // Logical work item: (kv head, head group) major, then items (prefill:
-  // row tiles longest first; split mode: see below).  With the remap, the
+  // row tiles longest first; split mode: split_item).  With the remap, the
   // blocks one XCD runs (blockIdx % 8 picks the XCD) come from one head
   // group, whose K/V then hit in that XCD's L2.  When a head group's tiles
   // fill m whole XCDs, its tiles, longest first, are dealt to them in
@@ -165,35 +134,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(const
       L = x * C + sl;
     }
   }
-  // Split mode: blocks [0, NH * F) are the whole splits (head group major,
-  // then stream, row tile, split); the rest are the streams' shorter last
-  // splits, longest first, all head groups of one before the next.
   int hgrp, si, tile, split;  // hgrp = kv head * (G / HW) + head group
   if (split_mode) {
-    const int NH = nb / A.total_tiles;
-    const int F = A.full_tiles;
-    if (L < NH * F) {
-      hgrp = L / F;
-      const int r = L - hgrp * F;
-      si = 0;
-      for (int i = 1; i < A.n_streams; ++i)
-        if (r >= A.s[i].full_begin) si = i;
-      const int nf = A.s[si].n_keys / A.split_keys;
-      const int local = r - A.s[si].full_begin;
-      tile = local / nf;
-      split = local - tile * nf;
-    } else {
-      const int j = L - NH * F;
-      hgrp = j % NH;
-      const int r = j / NH;
-      si = 0;
-      for (int i = 0; i < A.n_streams; ++i) {
-        const int pb = A.s[i].part_begin;
-        if (pb >= 0 && r >= pb && r < pb + (A.s[i].n_rows + rpt - 1) / rpt) si = i;
-      }
-      tile = r - A.s[si].part_begin;
-      split = A.s[si].n_splits - 1;
-    }
+    split_item(A, L, nb, hgrp, si, tile, split);
   } else {
     hgrp = L / A.total_tiles;
     const int it = A.total_tiles - 1 - L % A.total_tiles;

@@ -1,0 +1,543 @@
+// Split-K partials for decode streams with many (row, q head) columns and
+// fp8-e4m3 KV, for gfx950: speculative verify rows (for example 16 rows of a
+// 6-head group, 96 columns per kv head), causal or along a draft tree.
+//
+// Each workgroup computes the partial (m, l, o) of one split_keys-key split
+// for one kv head and every column of a row tile, reading the split's K and
+// V from HBM once, through the page table, one lookup per page (TensorFold
+// pull request #2011, "What this changes"); the merge kernel then combines
+// the splits (issue #1344, "Mechanism").  Rows may carry an ancestor table
+// (pull request #1355, follow-up checks, "Indexing").  The pages' fp8 tiles
+// and fp8 prompt kernel (pull request #1373, "What changes"; #2011, "Kernel
+// contract") multiply fp8 operands; so does this kernel.
+//
+// fp8 matrix cores.  Both products run on the E4M3 MFMAs, reading the stored
+// K and V codes as they are (no conversion):
+//   S^T = K Q^T   v_mfma_f32_16x16x128_f8f6f4, A = 16 keys x 128 dims of K;
+//   O^T += V^T P^T v_mfma_f32_32x32x64_f8f6f4, A = 32 dims x 64 keys of V.
+// Q and P, which are not fp8, are each carried as two E4M3 terms, x = hi + lo
+// with hi = E4M3(x) and lo = E4M3(x - hi), both rounded to nearest even:
+// about 8 significant bits, bf16's precision, for two products per term.
+//   * Q is scaled per column by a power of two sigma that puts max|q| below
+//     256 (bf16 Q then splits exactly); the logit scale becomes c / sigma.
+//   * P = 2^(s - m) is scaled by 2^6, so the weights that matter stay in
+//     E4M3's normal range.  With the scale, p <= 2^8 needs the running max m
+//     to lag the true maximum by at most 2 in log2 units: m moves when a
+//     logit passes it by more than that.  The partial then reports m - 6 as
+//     its reference logit, so every term 2^(s - m_ref) is still at most 2^8.
+//
+// Work split.  Eight waves, two per SIMD.  A step is 64 keys (a quarter of a
+// page, one fp8 V block).  SIMD s computes the logits of the step's keys
+// 16s .. 16s+15 (its two waves each for half of the columns), and the P.V
+// product for its D/4 dims (its two waves each for one 32-dim tile of every
+// column at head_dim 256, or half of the columns at 128).  Every K and V byte
+// of a step is read from LDS by one SIMD; the waves exchange P (two E4M3
+// terms, 64 keys x columns), the per-column maxima and, when a running max
+// moves, the rescale factors.
+//
+// Per step v the column maxima of S(v+1) are published together with P(v),
+// so one barrier per 64 keys serves every hand-off:
+//   O *= alpha(v-1) (rarely), O^T += V(v-1)^T P(v-1)^T   |  softmax(v): P(v)
+//   S(v+1) = K(v+1) Q^T, its column max over the wave's 16 keys
+//   -- barrier v --
+//
+// Loads.  Every wave issues its share of each step's DMAs into rings of four
+// K and four V stages: K(v+4) and V(v+2) in step v, each given about two and
+// a half steps to land; the waiting wave then passes the barrier that
+// publishes them (K(v+2) and V(v) are awaited before barrier v).
+//
+// LDS fragment orders (each lane's 16 bytes at lane*16, conflict-free):
+//   K entry b of lane (i, a): dims 64b + 16a .. +15 of key 16s + i; the QK
+//     operand of k-step kk is entries 2kk, 2kk+1, and Q's operand bytes
+//     follow the same dims;
+//   V entry b of lane (d, g): keys 32g + 16b .. +15 of dim d of the tile;
+//     P's operand bytes follow the same keys.
+#include "pa_device.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));      // one lane's 32 fp8 codes
+typedef float v4fe __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2fe __attribute__((ext_vector_type(2)));
+
+// C += A B on the fp8 matrix cores: E4M3FN A and B (format code 0), no
+// block scales.  Lane l holds row (A) or column (B) l % 16 (16x16x128) or
+// l % 32 (32x32x64) with 32 codes of the k range its lane group covers; A
+// and B take the same k order byte for byte, so any permutation of k shared
+// by both leaves the product unchanged.
+__device__ __forceinline__ v4f mfma8_16(v8i a, v8i b, v4f c) {
+  return __builtin_bit_cast(
+      v4f, __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, __builtin_bit_cast(v4fe, c), 0,
+                                                            0, 0, 0, 0, 0));
+}
+__device__ __forceinline__ v16f mfma8_32(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v8i join8(v4u x, v4u y) {
+  return v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+}
+
+// Four floats, each split into two E4M3FN terms x = hi + lo (RNE): the hi
+// codes in one dword (byte i for x_i), the lo codes in another.
+__device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, uint32_t& hi,
+                                       uint32_t& lo) {
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+  const v2fe b0 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+  const v2fe b1 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - b0[0], x1 - b0[1], 0, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - b1[0], x3 - b1[1], l, true);
+  hi = (uint32_t)h;
+  lo = (uint32_t)l;
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
+  constexpr int BK = 64;                     // keys per step
+  constexpr int NTG = 2 * verify_ntiles(D);  // 16-column n-tiles per workgroup (QK)
+  constexpr int NTW = NTG / 2;               // QK n-tiles per wave (a column half)
+  constexpr int CW = 16 * NTW;               // QK columns per wave
+  constexpr int NCOL = 16 * NTG;             // columns per workgroup
+  constexpr int KK = D / 128;                // QK k-steps
+  constexpr int KR = D / 64;                 // K entries per key row (64 dims each)
+  constexpr int DS = D / 4;                  // P.V dims per SIMD
+  constexpr int MTS = DS / 32;               // 32-dim P.V m-tiles per SIMD (2 or 1)
+  constexpr int NPV = NCOL / 32;             // 32-column P.V n-tiles per workgroup
+  constexpr int NPW = MTS == 2 ? NPV : NPV / 2;  // P.V n-tiles per wave
+  constexpr int TPW = D / 128;               // K (and V) DMA fragments per wave per step
+  constexpr int NK = 4, NV = 4;              // K and V ring stages
+  constexpr int STG = BK * D / 16;           // 16-byte entries per K (or V) stage
+  constexpr int PSL = 2 * NPV * 2 * 64;      // entries per P slot: [term][n-tile][half][lane]
+  constexpr int MXS = NCOL * 4;              // floats per maxima slot: [column][SIMD]
+  constexpr int ALS = NCOL + 8;              // floats per rescale slot: [column], 2 flags
+  constexpr float kPScale = 6.f;             // P carries a 2^6 scale (log2 units)
+  constexpr float kLag = 2.f;                // running max lags by at most this (log2 units)
+  static_assert(4 * KR * 64 == STG && 4 * MTS * 2 * 64 == STG, "a stage is 4 SIMDs' fragments");
+  static_assert(8 * TPW * 64 == STG, "eight waves share a stage's DMAs");
+  static_assert(kPage % BK == 0, "a step never straddles two pages");
+  static_assert(kPScale + kLag <= 8.f, "p <= 256 fits E4M3");
+  __shared__ v4u lds[(NK + NV) * STG + 2 * PSL + (3 * MXS + 2 * ALS) / 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = wave & 3;    // SIMD: key quarter of the S product, dim slice of P.V
+  const int hh = wave >> 2;  // column half (QK); dim tile or column half (P.V)
+  const int n = lane & 15;   // QK lane: column of an n-tile ...
+  const int a = lane >> 4;   // ... and its lane group
+  const int c32 = lane & 31; // P.V lane: column of a 32-column n-tile (or dim of V^T) ...
+  const int g32 = lane >> 5; // ... and its lane group
+  const int G = A.group;
+  const int HW = A.heads_per_wg;
+  const int rpt = A.rows_per_tile;
+
+  int hgrp, si, tile, split;
+  split_item(A, (int)blockIdx.x, (int)gridDim.x, hgrp, si, tile, split);
+  const int g = hgrp / (G / HW);
+  const int h0 = g * G + (hgrp % (G / HW)) * HW;
+  const StreamArg& S = A.s[si];
+  const int row0 = tile * rpt;
+  const int rows_here = min(rpt, S.n_rows - row0);
+  const int pos_first = S.first_pos + row0;
+  const int pos_last = pos_first + rows_here - 1;
+  const int n_keys_t = pos_last + 1;  // keys the tile's last row sees
+  const int k_lo = split * A.split_keys;
+  const int k_end = min(k_lo + A.split_keys, n_keys_t);
+  const int v_lo = k_lo / BK;
+  const int v_hi = k_end > k_lo ? (k_end + BK - 1) / BK : v_lo;
+  // first key some row of the tile may not see
+  const int mask_from = S.tree_mask ? S.first_pos : pos_first + 1;
+
+  struct Col {
+    int row, head, pos;
+    bool ok;
+  };
+  // Workgroup column cl: its (row, q head), recomputed where used.
+  auto col_of = [&](int cl) -> Col {
+    const int rl = cl / HW;
+    Col k;
+    k.head = h0 + (cl - rl * HW);
+    k.row = row0 + rl;
+    k.ok = rl < rows_here;
+    k.pos = k.ok ? S.first_pos + k.row : pos_last;
+    return k;
+  };
+  // QK column of this lane in n-tile nt (kept opaque so none of it stays live)
+  auto qcol = [&](int nt) -> int {
+    int ln = n;
+    asm("" : "+v"(ln));
+    return CW * hh + 16 * nt + ln;
+  };
+
+  const float c = A.scale_log2;
+  // Q^T operands (two E4M3 terms) of this wave's columns, and per column the
+  // logit scale c / sigma and the lag threshold in raw logit units.
+  v8i qh[NTW][KK], ql[NTW][KK];
+  float cc[NTW], thr[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const Col k = col_of(qcol(nt));
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(A.q) +
+                        ((int64_t)(S.row_offset + (k.ok ? k.row : row0)) * A.n_q_heads +
+                         (k.ok ? k.head : h0)) * D * 2;
+    // bytes 0..15 of k-step kk: dims 128kk + 16a + j; bytes 16..31: dims
+    // 128kk + 64 + 16a + j (four 16-byte loads of 8 bf16 each)
+    v4u raw[KK][4];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int q8 = 0; q8 < 2; ++q8) {
+          v4u x = load16(qp + (128 * kk + 64 * hf + 16 * a + 8 * q8) * 2);
+          if (!k.ok) x = v4u{0, 0, 0, 0};
+          raw[kk][2 * hf + q8] = x;
+        }
+    // element e (0, 1) of dword w (0..15) of k-step kk, as a float
+    auto f32 = [&](int kk, int w, int e) {
+      const uint32_t u = raw[kk][w >> 2][w & 3];
+      return __builtin_bit_cast(float, e ? (u & 0xFFFF0000u) : (u << 16));
+    };
+    float mx = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int w = 0; w < 16; ++w)
+        mx = fmaxf(mx, fmaxf(fabsf(f32(kk, w, 0)), fabsf(f32(kk, w, 1))));
+    mx = rows4_max(mx);
+    int e2 = 0;
+    (void)__builtin_frexpf(mx, &e2);  // mx < 2^e2 (e2 = 0 for a zero column)
+    const float sigma = __builtin_ldexpf(1.f, 8 - e2);
+    cc[nt] = __builtin_ldexpf(c, e2 - 8);
+    thr[nt] = kLag / cc[nt];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      uint32_t hw[8], lw[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        split4(f32(kk, 2 * w, 0) * sigma, f32(kk, 2 * w, 1) * sigma,
+               f32(kk, 2 * w + 1, 0) * sigma, f32(kk, 2 * w + 1, 1) * sigma, hw[w], lw[w]);
+      qh[nt][kk] = v8i{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5],
+                       (int)hw[6], (int)hw[7]};
+      ql[nt][kk] = v8i{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5],
+                       (int)lw[6], (int)lw[7]};
+    }
+  }
+
+  // Ancestor words of the QK columns' rows (all ones: the causal chain),
+  // read once: a global load inside the step loop would make the masked
+  // steps wait for every DMA in flight.
+  uint32_t anc[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const Col k = col_of(qcol(nt));
+    anc[nt] = (S.tree_mask && k.ok) ? S.tree_mask[k.row] : 0xFFFFFFFFu;
+  }
+
+  v4u* const Kring = lds;
+  v4u* const Vring = lds + NK * STG;
+  v4u* const Pring = Vring + NV * STG;
+  float* const Mx = reinterpret_cast<float*>(Pring + 2 * PSL);  // two maxima slots
+  float* const Ax = Mx + 2 * MXS;                                // two rescale slots
+  float* const Lx = Ax + 2 * ALS;                                // row sums at the end
+  typedef __attribute__((address_space(3))) v4u lds_v4u;
+
+  // Page tiles: the K loader runs ahead of the V loader and each keeps its
+  // own page, so every page is looked up once per loader.  Every wave loads
+  // a share of every step, so each wave sees every page id of the item.
+  PageTile TK{}, TV{};
+  int pk = -1, pvp = -1;
+  bool bad = false;
+  auto page_of = [&](int v, int& cur, PageTile& T) -> const PageTile& {
+    if ((v >> 2) != cur) {
+      cur = v >> 2;
+      T = page_tile<D, 1>(S, A.cache, cur, g);
+      bad |= !T.ok;
+    }
+    return T;
+  };
+  auto dma_k = [&](int v) {
+    const PageTile& T = page_of(v, pk, TK);
+    const auto rs = tile_rsrc(T.k, kPage * D);
+    v4u* dst = Kring + ((v - v_lo) & (NK - 1)) * STG;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int f = wave * TPW + i, sk = f / KR, b = f % KR;  // keys 16sk + n, dims 64b + 16a
+      dma16(rs, (16 * sk + n) * D + 64 * b + 16 * a, (v & 3) * BK * D, dst + f * 64);
+    }
+  };
+  auto dma_v = [&](int v) {
+    const PageTile& T = page_of(v, pvp, TV);
+    const auto rs = tile_rsrc(T.v, kPage * D);
+    v4u* dst = Vring + ((v - v_lo) & (NV - 1)) * STG;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      // SIMD sv, dim tile mt, half b: keys 32g + 16b .. of dim DS*sv + 32mt + d
+      const int f = wave * TPW + i, sv = f / (2 * MTS), mt = (f >> 1) % MTS, b = f & 1;
+      dma16(rs, (DS * sv + 32 * mt + c32) * 64 + 32 * g32 + 16 * b, (v & 3) * D * 64,
+            dst + f * 64);
+    }
+  };
+
+  // P.V accumulators: n-tile j of this wave is workgroup n-tile n0_w + j;
+  // lane (c, grp) holds rows (dims) 8q + 4grp + r of column c at index 4q + r.
+  const int mt_w = MTS == 2 ? hh : 0;        // this wave's P.V dim tile
+  const int n0_w = MTS == 2 ? 0 : hh * NPW;  // its first P.V n-tile
+  v16f o[NPW];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) o[j] = v16f{};
+  float m_run[NTW], l_part[NTW], mc[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_part[nt] = 0.f;
+    mc[nt] = 0.f;
+  }
+
+  // S(u) = K(u) Q^T for this SIMD's 16 keys, then the mask (steps that
+  // reach a row's own keys or the stream's end) and the per-column max over
+  // the 16 keys, written to the maxima slot of step u.
+  auto qk = [&](int u, v4f (&Sx)[NTW]) {
+    const lds_v4u* Lk =
+        (const lds_v4u*)(Kring + ((u - v_lo) & (NK - 1)) * STG + s * KR * 64 + lane);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) Sx[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const v8i ka = join8(Lk[(2 * kk) * 64], Lk[(2 * kk + 1) * 64]);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        Sx[nt] = mfma8_16(ka, qh[nt][kk], Sx[nt]);
+        Sx[nt] = mfma8_16(ka, ql[nt][kk], Sx[nt]);
+      }
+    }
+    if (u * BK + BK - 1 >= mask_from) {
+      // lane (n, a) holds keys 16s + 4a + i of the step for its column
+      const int kabs0 = u * BK + 16 * s + 4 * a;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const Col k = col_of(qcol(nt));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kabs = kabs0 + i, rel = kabs - S.first_pos;
+          const bool anc_ok = (rel < 0) | (((anc[nt] >> (rel & 31)) & 1u) != 0u);
+          const bool vis = (kabs <= k.pos) & anc_ok;
+          Sx[nt][i] = vis ? Sx[nt][i] : -INFINITY;
+        }
+      }
+    }
+    float* mx = Mx + ((u - v_lo) & 1) * MXS;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const float m4 = fmaxf(fmaxf(Sx[nt][0], Sx[nt][1]), fmaxf(Sx[nt][2], Sx[nt][3]));
+      const float m = rows4_max(m4);
+      if (a == 0) mx[qcol(nt) * 4 + s] = m;
+    }
+  };
+
+  // Softmax of step v from S(v) and the step's maxima (published by barrier
+  // v-1): the running max (moved only past the lag), on a move the rescale
+  // factors (published for the P.V of step v, with a flag per column half),
+  // the row-sum partials, and P(v) as two E4M3 terms into P slot (v & 1).
+  auto softmax = [&](int v, v4f (&Sx)[NTW]) {
+    const float* mxs = Mx + ((v - v_lo) & 1) * MXS;
+    float* al = Ax + ((v - v_lo) & 1) * ALS;
+    float m[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const v4f m4 = *reinterpret_cast<const v4f*>(mxs + qcol(nt) * 4);
+      m[nt] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    }
+    bool mv = false;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) mv |= m[nt] > m_run[nt] + thr[nt];
+    // every wave of a column half reads the same maxima, so all of them
+    // take the same branch and reach the same running max
+    if (__any(mv)) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        float mu = m_run[nt];
+        if (m[nt] > mu + thr[nt]) mu = m[nt];
+        const float alpha =
+            mu == m_run[nt] ? 1.f : __builtin_amdgcn_exp2f((m_run[nt] - mu) * cc[nt]);
+        m_run[nt] = mu;
+        mc[nt] = mu == -INFINITY ? 0.f : mu * cc[nt] - kPScale;
+        l_part[nt] *= alpha;
+        if (s == 0 && a == 0) al[qcol(nt)] = alpha;
+      }
+      if (s == 0 && lane == 0) al[NCOL + hh] = 1.f;
+    } else {
+      if (s == 0 && lane == 0) al[NCOL + hh] = 0.f;
+    }
+    v4u* pd = Pring + ((v - v_lo) & 1) * PSL;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sx[nt][i], cc[nt], -mc[nt]));
+      l_part[nt] += (p[0] + p[1]) + (p[2] + p[3]);
+      uint32_t hi, lo;
+      split4(p[0], p[1], p[2], p[3], hi, lo);
+      // key 16s + 4a + i = 32 gp + 16 bp + 4a + i: dword a of the P.V operand
+      // entry (half bp) of lane (column % 32, gp)
+      const int cl = qcol(nt);
+      const int N = cl >> 5, e = (cl & 31) + 32 * (s >> 1), bp = s & 1;
+      uint32_t* dh = reinterpret_cast<uint32_t*>(pd + ((0 * NPV + N) * 2 + bp) * 64 + e);
+      uint32_t* dl = reinterpret_cast<uint32_t*>(pd + ((1 * NPV + N) * 2 + bp) * 64 + e);
+      dh[a] = hi;
+      dl[a] = lo;
+    }
+  };
+
+  // O^T += V(u)^T P(u)^T over step u's 64 keys for this wave's dims and
+  // columns, after the rescale of step u (published by barrier u).
+  auto pv = [&](int u, bool tail) {
+    const float* al = Ax + ((u - v_lo) & 1) * ALS;
+    const float fl0 = al[NCOL], fl1 = al[NCOL + 1];
+    if (fl0 != 0.f || fl1 != 0.f) {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        const int cl = 32 * (n0_w + j) + c32;
+        const float f = (cl < CW ? fl0 : fl1) != 0.f ? al[cl] : 1.f;
+        o[j] *= f;
+      }
+    }
+    const lds_v4u* Lv = (const lds_v4u*)(Vring + ((u - v_lo) & (NV - 1)) * STG +
+                                         (s * MTS + mt_w) * 2 * 64 + lane);
+    v4u x0 = Lv[0], x1 = Lv[64];
+    if (tail) {
+      // the stream's last step may run past its last key: those values
+      // (unwritten slots, possibly NaN codes) become zeros
+      const int k0 = u * BK + 32 * g32;
+      x0 = keep_first_b(x0, n_keys_t - k0);
+      x1 = keep_first_b(x1, n_keys_t - k0 - 16);
+    }
+    const v8i va = join8(x0, x1);
+    const lds_v4u* Lp = (const lds_v4u*)(Pring + ((u - v_lo) & 1) * PSL + lane);
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+      const int N = n0_w + j;
+      const v8i ph = join8(Lp[((0 * NPV + N) * 2 + 0) * 64], Lp[((0 * NPV + N) * 2 + 1) * 64]);
+      const v8i pl = join8(Lp[((1 * NPV + N) * 2 + 0) * 64], Lp[((1 * NPV + N) * 2 + 1) * 64]);
+      o[j] = mfma8_32(va, ph, o[j]);
+      o[j] = mfma8_32(va, pl, o[j]);
+    }
+  };
+
+  // Wait until this wave's DMAs of K(v+2) and V(v) have landed: at most the
+  // tiles issued after V(v) (K(v+3), V(v+1), K(v+4), V(v+2), those that
+  // exist) may still be in flight.
+  auto wait_step = [&](int v) {
+    const int later = (v + 3 < v_hi) + (v + 1 < v_hi) + (v + 4 < v_hi) + (v + 2 < v_hi);
+    if (later == 4) wait_vmem<4 * TPW>();
+    else if (later == 3) wait_vmem<3 * TPW>();
+    else if (later == 2) wait_vmem<2 * TPW>();
+    else if (later == 1) wait_vmem<TPW>();
+    else wait_vmem<0>();
+  };
+
+  if (v_hi > v_lo) {
+    // Prologue, in the order the steady state expects: K(v_lo), K(v_lo+1);
+    // then as "step v_lo-2" K(v_lo+2), V(v_lo), and as "step v_lo-1"
+    // K(v_lo+3), V(v_lo+1).
+    const int n_st = v_hi - v_lo;
+    dma_k(v_lo);
+    if (n_st > 1) dma_k(v_lo + 1);
+    if (n_st > 2) dma_k(v_lo + 2);
+    dma_v(v_lo);
+    if (n_st > 3) dma_k(v_lo + 3);
+    if (n_st > 1) dma_v(v_lo + 1);
+    // K(v_lo) and K(v_lo+1) landed: after them at most K(v_lo+2), V(v_lo),
+    // K(v_lo+3), V(v_lo+1) remain
+    {
+      const int later = (n_st > 2) + 1 + (n_st > 3) + (n_st > 1);
+      if (later == 4) wait_vmem<4 * TPW>();
+      else if (later == 3) wait_vmem<3 * TPW>();
+      else if (later == 2) wait_vmem<2 * TPW>();
+      else wait_vmem<TPW>();
+    }
+    lds_barrier();
+    v4f Sc[NTW], Sn[NTW];
+    qk(v_lo, Sc);
+    lds_barrier();  // publishes the maxima of S(v_lo)
+
+    // Interval v runs between barriers v-1 and v: the DMAs of K(v+4) and
+    // V(v+2), the P.V of step v-1, the softmax of step v and S(v+1).  The
+    // last interval (v = v_hi) is P.V only.
+    for (int v = v_lo; v <= v_hi; ++v) {
+      if (v + 4 < v_hi) dma_k(v + 4);
+      if (v + 2 < v_hi) dma_v(v + 2);
+      if (v > v_lo) pv(v - 1, v == v_hi && (v - 1) * BK + BK > n_keys_t);
+      if (v == v_hi) break;
+      softmax(v, Sc);
+      if (v + 1 < v_hi) qk(v + 1, Sn);
+      wait_step(v);
+      lds_barrier();  // publishes P(v), the rescale of v, the maxima of S(v+1), K(v+2), V(v)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) Sc[nt] = Sn[nt];
+    }
+  }
+
+  // Row sums: each wave's partial over its keys (summed across the column's
+  // four lane groups), then, for every column, the four SIMDs' sums in SIMD
+  // order.
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const float l = rows4_sum(l_part[nt]);
+    if (a == 0) Lx[qcol(nt) * 4 + s] = l;
+  }
+  lds_barrier();
+  if (s == 0 && a == 0) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const Col k = col_of(qcol(nt));
+      if (!k.ok) continue;
+      const int64_t slot =
+          S.slot_base + ((int64_t)k.row * A.n_q_heads + k.head) * S.n_splits + split;
+      const v4f l4 = *reinterpret_cast<const v4f*>(Lx + qcol(nt) * 4);
+      // p was exp2(s*c - (m_run*c - 6)): the split's reference logit in log2
+      // units is m_run*c - 6; a rejected page id poisons it as a NaN
+      const float mref = m_run[nt] == -INFINITY ? -INFINITY : m_run[nt] * cc[nt] - kPScale;
+      A.ws_ml[2 * slot] = bad ? __builtin_nanf("") : mref;
+      A.ws_ml[2 * slot + 1] = ((l4[0] + l4[1]) + l4[2]) + l4[3];
+    }
+  }
+  // o: lane (c, grp) of n-tile j holds dims DS*s + 32mt + 8q + 4grp + r
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const Col k = col_of(32 * (n0_w + j) + c32);
+    if (!k.ok) continue;
+    const int64_t slot =
+        S.slot_base + ((int64_t)k.row * A.n_q_heads + k.head) * S.n_splits + split;
+    float* dst = A.ws_o + slot * D + DS * s + 32 * mt_w + 4 * g32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<v4f*>(dst + 8 * q) =
+          v4f{o[j][4 * q], o[j][4 * q + 1], o[j][4 * q + 2], o[j][4 * q + 3]};
+  }
+}
+
+template <int D>
+static int launch_verify_t(const PrefillArgs& A, hipStream_t st) {
+  dim3 grid((unsigned)(A.total_tiles * A.cache.n_kv_heads * (A.group / A.heads_per_wg)));
+  hipLaunchKernelGGL((verify_kernel<D>), grid, dim3(512), 0, st, A);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int verify_wg_columns(int head_dim) { return 2 * 16 * verify_ntiles(head_dim); }
+
+int launch_verify(const PrefillArgs& A, int head_dim, hipStream_t st) {
+  if (head_dim == 128) return launch_verify_t<128>(A, st);
+  if (head_dim == 256) return launch_verify_t<256>(A, st);
+  return -7;
+}
+
+}  // namespace pa
