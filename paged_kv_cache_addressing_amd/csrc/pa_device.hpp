@@ -195,6 +195,44 @@ __device__ __forceinline__ PageTile page_tile(const StreamArg& s, const CacheArg
   return r;
 }
 
+// The page-tile map of one (stream, kv head), with the stream's fields held
+// in registers for the whole work item: tile t of a paged stream is page
+// PT[t] (read by the caller, a wave-uniform scalar load), of a slab the t-th
+// run of 256 positions.  Same addresses as page_tile.
+template <int D, int ESZ>
+struct TileMap {
+  const int32_t* pt;
+  uint8_t* kb;     // K of the kv head in page 0 (paged) or at position 0 (slab)
+  uint8_t* vb;
+  int64_t stride;  // bytes between pages (paged) or 256-position runs (slab)
+  int32_t n_pages;
+  bool paged;
+  __device__ __forceinline__ TileMap(const StreamArg& s, const CacheArg& c, int g) {
+    paged = s.layout == 0;
+    pt = s.page_table;
+    n_pages = c.n_pages;
+    const int64_t off = (int64_t)g * (paged ? kPage : s.slab_cap) * D * ESZ;
+    kb = s.k_base + off;
+    vb = s.v_base + off;
+    stride = paged ? c.page_stride * ESZ : (int64_t)kPage * D * ESZ;
+  }
+  // Page id of tile t (paged streams; loads through the constant address
+  // space, tracked by lgkmcnt, so it never waits on vector loads).
+  __device__ __forceinline__ int32_t id(int t) const {
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    return paged ? ((const_i32*)pt)[t] : t;
+  }
+  // The tile given its page id (or, for a slab, its index).
+  __device__ __forceinline__ PageTile tile(int32_t idv) const {
+    PageTile r;
+    r.ok = !paged || (uint32_t)idv < (uint32_t)n_pages;
+    const int64_t off = (int64_t)(r.ok ? idv : 0) * stride;
+    r.k = kb + off;
+    r.v = vb + off;
+    return r;
+  }
+};
+
 // Index of the stream that owns launch-local work item `x`: the last stream
 // whose `begin` is <= x (streams with no work are never placed in a launch).
 template <int FIELD>

@@ -20,11 +20,11 @@
 // about 8 significant bits, bf16's precision, for two products per term.
 //   * Q is scaled per column by a power of two sigma that puts max|q| below
 //     256 (bf16 Q then splits exactly); the logit scale becomes c / sigma.
-//   * P = 2^(s - m) is scaled by 2^6, so the weights that matter stay in
-//     E4M3's normal range.  With the scale, p <= 2^8 needs the running max m
-//     to lag the true maximum by at most 2 in log2 units: m moves when a
-//     logit passes it by more than that.  The partial then reports m - 6 as
-//     its reference logit, so every term 2^(s - m_ref) is still at most 2^8.
+//   * P = 2^(s - m) is scaled by 2^4, so the weights that matter stay in
+//     E4M3's normal range.  The running max m may lag the true maximum by up
+//     to 4 in log2 units (p <= 2^8 then): m moves only when a logit passes
+//     it by more than that.  The partial reports m - 4 as its reference
+//     logit, so every term 2^(s - m_ref) is still at most 2^8.
 //
 // Work split.  Eight waves, two per SIMD.  A step is 64 keys (a quarter of a
 // page, one fp8 V block).  SIMD s computes the logits of the step's keys
@@ -32,14 +32,20 @@
 // product for its D/4 dims (its two waves each for one 32-dim tile of every
 // column at head_dim 256, or half of the columns at 128).  Every K and V byte
 // of a step is read from LDS by one SIMD; the waves exchange P (two E4M3
-// terms, 64 keys x columns), the per-column maxima and, when a running max
-// moves, the rescale factors.
+// terms, 64 keys x columns) and one overflow flag per wave.
 //
-// Per step v the column maxima of S(v+1) are published together with P(v),
-// so one barrier per 64 keys serves every hand-off:
-//   O *= alpha(v-1) (rarely), O^T += V(v-1)^T P(v-1)^T   |  softmax(v): P(v)
-//   S(v+1) = K(v+1) Q^T, its column max over the wave's 16 keys
+// Running max.  Each wave computes P(v) with the running max as it stands
+// and flags the step when one of its logits passes that max by more than
+// the lag.  The flags travel with P(v), so one barrier per 64 keys serves
+// every hand-off:
+//   check of step v-1, O^T += V(v-1)^T P(v-1)^T  |  softmax(v): P(v), flag
+//   S(v+1) = K(v+1) Q^T
 //   -- barrier v --
+// Only when a flag is set (in the first step of a split, then in well under
+// one step in a hundred on random data) do the waves exchange the step's
+// column maxima, move the maxima that passed, rescale the row sums and O,
+// and recompute P(v-1): two more barriers.  With a lag of 2 instead of 4,
+// some column of a 96-column tile moves in about half of all steps.
 //
 // Loads.  Every wave issues its share of each step's DMAs into rings of four
 // K and four V stages: K(v+4) and V(v+2) in step v, each given about two and
@@ -115,15 +121,14 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   constexpr int NK = 4, NV = 4;              // K and V ring stages
   constexpr int STG = BK * D / 16;           // 16-byte entries per K (or V) stage
   constexpr int PSL = 2 * NPV * 2 * 64;      // entries per P slot: [term][n-tile][half][lane]
-  constexpr int MXS = NCOL * 4;              // floats per maxima slot: [column][SIMD]
-  constexpr int ALS = NCOL + 8;              // floats per rescale slot: [column], 2 flags
-  constexpr float kPScale = 6.f;             // P carries a 2^6 scale (log2 units)
-  constexpr float kLag = 2.f;                // running max lags by at most this (log2 units)
+  constexpr int MXS = NCOL * 4;              // floats of the maxima: [column][SIMD]
+  constexpr float kPScale = 4.f;             // P carries a 2^4 scale (log2 units)
+  constexpr float kLag = 4.f;                // running max lags by at most this (log2 units)
   static_assert(4 * KR * 64 == STG && 4 * MTS * 2 * 64 == STG, "a stage is 4 SIMDs' fragments");
   static_assert(8 * TPW * 64 == STG, "eight waves share a stage's DMAs");
   static_assert(kPage % BK == 0, "a step never straddles two pages");
   static_assert(kPScale + kLag <= 8.f, "p <= 256 fits E4M3");
-  __shared__ v4u lds[(NK + NV) * STG + 2 * PSL + (3 * MXS + 2 * ALS) / 4];
+  __shared__ v4u lds[(NK + NV) * STG + 2 * PSL + (MXS + 2 * NCOL + 4) / 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   // Q^T operands (two E4M3 terms) of this wave's columns, and per column the
   // logit scale c / sigma and the lag threshold in raw logit units.
   v8i qh[NTW][KK], ql[NTW][KK];
-  float cc[NTW], thr[NTW];
+  float cc[NTW];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const Col k = col_of(qcol(nt));
@@ -216,7 +221,6 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
     (void)__builtin_frexpf(mx, &e2);  // mx < 2^e2 (e2 = 0 for a zero column)
     const float sigma = __builtin_ldexpf(1.f, 8 - e2);
     cc[nt] = __builtin_ldexpf(c, e2 - 8);
-    thr[nt] = kLag / cc[nt];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       uint32_t hw[8], lw[8];
@@ -231,40 +235,51 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
     }
   }
 
-  // Ancestor words of the QK columns' rows (all ones: the causal chain),
-  // read once: a global load inside the step loop would make the masked
-  // steps wait for every DMA in flight.
-  uint32_t anc[NTW];
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const Col k = col_of(qcol(nt));
-    anc[nt] = (S.tree_mask && k.ok) ? S.tree_mask[k.row] : 0xFFFFFFFFu;
-  }
-
   v4u* const Kring = lds;
   v4u* const Vring = lds + NK * STG;
   v4u* const Pring = Vring + NV * STG;
-  float* const Mx = reinterpret_cast<float*>(Pring + 2 * PSL);  // two maxima slots
-  float* const Ax = Mx + 2 * MXS;                                // two rescale slots
-  float* const Lx = Ax + 2 * ALS;                                // row sums at the end
+  float* const Mx = reinterpret_cast<float*>(Pring + 2 * PSL);  // maxima, at the end row sums
+  float* const Al = Mx + MXS;                                    // rescale factors
+  uint32_t* const Anc = reinterpret_cast<uint32_t*>(Al + NCOL);  // ancestor words [column]
+  uint8_t* const Fb = reinterpret_cast<uint8_t*>(Anc + NCOL);      // overflow flags [slot][wave]
+
+  // Ancestor words of the QK columns' rows (all ones: the causal chain),
+  // read once into LDS: a global load inside the step loop would make the
+  // masked steps wait for every DMA in flight.
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const Col k = col_of(qcol(nt));
+    if (s == 0 && a == 0) Anc[qcol(nt)] = (S.tree_mask && k.ok) ? S.tree_mask[k.row] : 0xFFFFFFFFu;
+  }
   typedef __attribute__((address_space(3))) v4u lds_v4u;
 
-  // Page tiles: the K loader runs ahead of the V loader and each keeps its
-  // own page, so every page is looked up once per loader.  Every wave loads
-  // a share of every step, so each wave sees every page id of the item.
-  PageTile TK{}, TV{};
-  int pk = -1, pvp = -1;
+  // Page tiles.  The stream's fields stay in registers (TileMap), and the
+  // page ids are read one page ahead: the id of the K loader's next page is
+  // loaded when its current page starts, four steps before it is needed.  The
+  // V loader runs two steps behind the K loader, so its page is the K
+  // loader's current or previous one.  Every wave loads a share of every
+  // step, so each wave sees every page id of the item.
+  const TileMap<D, 1> map(S, A.cache, g);
+  const int t_last = v_hi > v_lo ? (v_hi - 1) >> 2 : v_lo >> 2;  // last page of the item
+  PageTile TK{}, TKprev{};
+  int pk = -1;
+  int32_t next_id = 0;
   bool bad = false;
-  auto page_of = [&](int v, int& cur, PageTile& T) -> const PageTile& {
-    if ((v >> 2) != cur) {
-      cur = v >> 2;
-      T = page_tile<D, 1>(S, A.cache, cur, g);
-      bad |= !T.ok;
+  auto page_k = [&](int v) -> const PageTile& {
+    const int t = v >> 2;
+    if (t != pk) {
+      const int32_t idv = pk < 0 ? map.id(t) : next_id;
+      next_id = map.id(min(t + 1, t_last));
+      TKprev = TK;
+      TK = map.tile(idv);
+      bad |= !TK.ok;
+      pk = t;
     }
-    return T;
+    return TK;
   };
+  auto page_v = [&](int v) -> const PageTile& { return (v >> 2) == pk ? TK : TKprev; };
   auto dma_k = [&](int v) {
-    const PageTile& T = page_of(v, pk, TK);
+    const PageTile& T = page_k(v);
     const auto rs = tile_rsrc(T.k, kPage * D);
     v4u* dst = Kring + ((v - v_lo) & (NK - 1)) * STG;
 #pragma unroll
@@ -274,7 +289,7 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
     }
   };
   auto dma_v = [&](int v) {
-    const PageTile& T = page_of(v, pvp, TV);
+    const PageTile& T = page_v(v);
     const auto rs = tile_rsrc(T.v, kPage * D);
     v4u* dst = Vring + ((v - v_lo) & (NV - 1)) * STG;
 #pragma unroll
@@ -293,18 +308,26 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   v16f o[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) o[j] = v16f{};
-  float m_run[NTW], l_part[NTW], mc[NTW];
+  // Per column: the exponent offset mc (log2 units, the same in every wave of
+  // the column; -FLT_MAX until the column has seen a key), so that
+  // p = 2^(s*cc - mc); the row-sum partial; the last step's row-sum terms.
+  // mc is the running max (in log2 units) less the scale of P (kPScale); it
+  // moves when some p = 2^(s*cc - mc) would exceed 2^(kPScale + kLag).
+  constexpr float kNoMax = -3.40282347e38f;
+  float mc[NTW], l_part[NTW], lp[NTW];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
-    m_run[nt] = -INFINITY;
+    mc[nt] = kNoMax;
     l_part[nt] = 0.f;
-    mc[nt] = 0.f;
+    lp[nt] = 0.f;
   }
 
-  // S(u) = K(u) Q^T for this SIMD's 16 keys, then the mask (steps that
-  // reach a row's own keys or the stream's end) and the per-column max over
-  // the 16 keys, written to the maxima slot of step u.
-  auto qk = [&](int u, v4f (&Sx)[NTW]) {
+  // Scheduling groups (__builtin_amdgcn_sched_group_barrier masks).
+  constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+
+  // S(u) = K(u) Q^T for this SIMD's 16 keys, then, in the steps that reach a
+  // row's own keys or the stream's end, the mask.
+  auto qk = [&](int u, v4f (&Sx)[NTW]) __attribute__((always_inline)) {
     const lds_v4u* Lk =
         (const lds_v4u*)(Kring + ((u - v_lo) & (NK - 1)) * STG + s * KR * 64 + lane);
 #pragma unroll
@@ -319,71 +342,42 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
       }
     }
     if (u * BK + BK - 1 >= mask_from) {
+      // kept a branch (the empty volatile asm cannot be speculated): the
+      // selects would otherwise run on every step
+      asm volatile("");
       // lane (n, a) holds keys 16s + 4a + i of the step for its column
       const int kabs0 = u * BK + 16 * s + 4 * a;
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         const Col k = col_of(qcol(nt));
+        const uint32_t anc = Anc[qcol(nt)];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kabs = kabs0 + i, rel = kabs - S.first_pos;
-          const bool anc_ok = (rel < 0) | (((anc[nt] >> (rel & 31)) & 1u) != 0u);
+          const bool anc_ok = (rel < 0) | (((anc >> (rel & 31)) & 1u) != 0u);
           const bool vis = (kabs <= k.pos) & anc_ok;
           Sx[nt][i] = vis ? Sx[nt][i] : -INFINITY;
         }
       }
     }
-    float* mx = Mx + ((u - v_lo) & 1) * MXS;
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const float m4 = fmaxf(fmaxf(Sx[nt][0], Sx[nt][1]), fmaxf(Sx[nt][2], Sx[nt][3]));
-      const float m = rows4_max(m4);
-      if (a == 0) mx[qcol(nt) * 4 + s] = m;
-    }
   };
 
-  // Softmax of step v from S(v) and the step's maxima (published by barrier
-  // v-1): the running max (moved only past the lag), on a move the rescale
-  // factors (published for the P.V of step v, with a flag per column half),
-  // the row-sum partials, and P(v) as two E4M3 terms into P slot (v & 1).
-  auto softmax = [&](int v, v4f (&Sx)[NTW]) {
-    const float* mxs = Mx + ((v - v_lo) & 1) * MXS;
-    float* al = Ax + ((v - v_lo) & 1) * ALS;
-    float m[NTW];
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const v4f m4 = *reinterpret_cast<const v4f*>(mxs + qcol(nt) * 4);
-      m[nt] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    }
-    bool mv = false;
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) mv |= m[nt] > m_run[nt] + thr[nt];
-    // every wave of a column half reads the same maxima, so all of them
-    // take the same branch and reach the same running max
-    if (__any(mv)) {
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        float mu = m_run[nt];
-        if (m[nt] > mu + thr[nt]) mu = m[nt];
-        const float alpha =
-            mu == m_run[nt] ? 1.f : __builtin_amdgcn_exp2f((m_run[nt] - mu) * cc[nt]);
-        m_run[nt] = mu;
-        mc[nt] = mu == -INFINITY ? 0.f : mu * cc[nt] - kPScale;
-        l_part[nt] *= alpha;
-        if (s == 0 && a == 0) al[qcol(nt)] = alpha;
-      }
-      if (s == 0 && lane == 0) al[NCOL + hh] = 1.f;
-    } else {
-      if (s == 0 && lane == 0) al[NCOL + hh] = 0.f;
-    }
+  // Softmax of step v with the running max as it stands: P(v) as two E4M3
+  // terms into P slot (v & 1), the row-sum terms lp, and (when `flag`) this
+  // wave's overflow flag: some logit of its keys above the running max by
+  // more than the lag, so that P(v) may not fit the scale.
+  auto soft = [&](int v, const v4f (&Sx)[NTW], bool flag) __attribute__((always_inline)) {
     v4u* pd = Pring + ((v - v_lo) & 1) * PSL;
+    bool ov = false;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
-      float p[4];
+      float t[4], p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sx[nt][i], cc[nt], -mc[nt]));
-      l_part[nt] += (p[0] + p[1]) + (p[2] + p[3]);
+      for (int i = 0; i < 4; ++i) {
+        t[i] = __builtin_fmaf(Sx[nt][i], cc[nt], -mc[nt]);
+        p[i] = __builtin_amdgcn_exp2f(t[i]);
+      }
+      lp[nt] = (p[0] + p[1]) + (p[2] + p[3]);
       uint32_t hi, lo;
       split4(p[0], p[1], p[2], p[3], hi, lo);
       // key 16s + 4a + i = 32 gp + 16 bp + 4a + i: dword a of the P.V operand
@@ -394,22 +388,59 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
       uint32_t* dl = reinterpret_cast<uint32_t*>(pd + ((1 * NPV + N) * 2 + bp) * 64 + e);
       dh[a] = hi;
       dl[a] = lo;
+      ov |= fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])) > kPScale + kLag;
+    }
+    if (flag) {
+      const bool any = __any(ov);
+      if (lane == 0) Fb[((v - v_lo) & 1) * 8 + wave] = any ? 1 : 0;
     }
   };
 
-  // O^T += V(u)^T P(u)^T over step u's 64 keys for this wave's dims and
-  // columns, after the rescale of step u (published by barrier u).
-  auto pv = [&](int u, bool tail) {
-    const float* al = Ax + ((u - v_lo) & 1) * ALS;
-    const float fl0 = al[NCOL], fl1 = al[NCOL + 1];
-    if (fl0 != 0.f || fl1 != 0.f) {
+  // Step u overflowed in some wave: every wave takes this path (they all
+  // read the same flags).  The column maxima of the step are exchanged; a
+  // column whose maximum passed its running max by more than the lag moves
+  // it there; the row sums and (after the second barrier) the P.V
+  // accumulators are rescaled, and P(u) and its row-sum terms recomputed.
+  auto redo = [&](int u, const v4f (&Sx)[NTW]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < NPW; ++j) {
-        const int cl = 32 * (n0_w + j) + c32;
-        const float f = (cl < CW ? fl0 : fl1) != 0.f ? al[cl] : 1.f;
-        o[j] *= f;
-      }
+    for (int nt = 0; nt < NTW; ++nt) {
+      const float m4 = fmaxf(fmaxf(Sx[nt][0], Sx[nt][1]), fmaxf(Sx[nt][2], Sx[nt][3]));
+      const float m = rows4_max(m4);
+      if (a == 0) Mx[qcol(nt) * 4 + s] = m;
     }
+    lds_barrier();  // publishes the maxima
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const v4f m4 = *reinterpret_cast<const v4f*>(Mx + qcol(nt) * 4);
+      const float m = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      float alpha = 1.f;
+      if (__builtin_fmaf(m, cc[nt], -mc[nt]) > kPScale + kLag) {
+        const float mn = m * cc[nt] - kPScale;
+        alpha = __builtin_amdgcn_exp2f(mc[nt] - mn);  // 0 for a column's first keys
+        mc[nt] = mn;
+      }
+      l_part[nt] *= alpha;
+      if (s == 0 && a == 0) Al[qcol(nt)] = alpha;
+    }
+    soft(u, Sx, false);
+    lds_barrier();  // publishes P(u) and the rescale factors
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) o[j] *= Al[32 * (n0_w + j) + c32];
+  };
+
+  // Before the P.V of step u: the overflow flags of step u (published by
+  // barrier u), the slow path when any is set, then the row sums.
+  auto check = [&](int u, const v4f (&Sx)[NTW]) __attribute__((always_inline)) {
+    const uint64_t f = *reinterpret_cast<const uint64_t*>(Fb + ((u - v_lo) & 1) * 8);
+    const uint32_t any = __builtin_amdgcn_readfirstlane((uint32_t)f | (uint32_t)(f >> 32));
+    if (any != 0) redo(u, Sx);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) l_part[nt] += lp[nt];
+  };
+
+  // P.V of step u (O^T += V(u)^T P(u)^T over its 64 keys for this wave's
+  // dims and columns): pv_prep reads the V operand, pv_body multiplies.
+  auto pv_prep = [&](int u, bool tail) -> v8i {
     const lds_v4u* Lv = (const lds_v4u*)(Vring + ((u - v_lo) & (NV - 1)) * STG +
                                          (s * MTS + mt_w) * 2 * 64 + lane);
     v4u x0 = Lv[0], x1 = Lv[64];
@@ -420,7 +451,9 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
       x0 = keep_first_b(x0, n_keys_t - k0);
       x1 = keep_first_b(x1, n_keys_t - k0 - 16);
     }
-    const v8i va = join8(x0, x1);
+    return join8(x0, x1);
+  };
+  auto pv_body = [&](int u, const v8i& va) {
     const lds_v4u* Lp = (const lds_v4u*)(Pring + ((u - v_lo) & 1) * PSL + lane);
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
@@ -465,25 +498,79 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
       else wait_vmem<TPW>();
     }
     lds_barrier();
-    v4f Sc[NTW], Sn[NTW];
-    qk(v_lo, Sc);
-    lds_barrier();  // publishes the maxima of S(v_lo)
+    // The logits of two steps are live at a time: in interval v those of
+    // step v-1 (for the slow path of its check) and of step v, and S(v+1)
+    // takes step v-1's registers once that check is done.  Intervals run in
+    // pairs with the two buffers' roles swapped.
+    v4f B0[NTW], B1[NTW];
+    qk(v_lo, B0);
+    lds_barrier();  // every wave is done with K(v_lo) before K(v_lo+4) reuses its stage
 
     // Interval v runs between barriers v-1 and v: the DMAs of K(v+4) and
-    // V(v+2), the P.V of step v-1, the softmax of step v and S(v+1).  The
-    // last interval (v = v_hi) is P.V only.
-    for (int v = v_lo; v <= v_hi; ++v) {
+    // V(v+2), the check and the P.V of step v-1, the softmax of step v and
+    // S(v+1).
+    auto steady = [&](int v, v4f (&X)[NTW], v4f (&Y)[NTW]) __attribute__((always_inline)) {
+      check(v - 1, X);
+      const v8i va = pv_prep(v - 1, false);
       if (v + 4 < v_hi) dma_k(v + 4);
-      if (v + 2 < v_hi) dma_v(v + 2);
-      if (v > v_lo) pv(v - 1, v == v_hi && (v - 1) * BK + BK > n_keys_t);
-      if (v == v_hi) break;
-      softmax(v, Sc);
-      if (v + 1 < v_hi) qk(v + 1, Sn);
-      wait_step(v);
-      lds_barrier();  // publishes P(v), the rescale of v, the maxima of S(v+1), K(v+2), V(v)
+      // the P.V products of step v-1 and the softmax of step v: one
+      // branch-free block, each MFMA followed by a share of the VALU work
+      pv_body(v - 1, va);
+      soft(v, Y, true);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 1);
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) Sc[nt] = Sn[nt];
+      for (int i = 0; i < 2 * NPW; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kValu, 10, 1);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (v + 2 < v_hi) dma_v(v + 2);
+      qk(v + 1, X);
+      wait_step(v);
+      lds_barrier();  // publishes P(v), its flags, K(v+2), V(v)
+    };
+
+    // interval v_lo: no P.V yet
+    if (v_lo + 4 < v_hi) dma_k(v_lo + 4);
+    if (v_lo + 2 < v_hi) dma_v(v_lo + 2);
+    soft(v_lo, B0, true);
+    if (v_lo + 1 < v_hi) {
+      qk(v_lo + 1, B1);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) B1[nt] = B0[nt];  // the last step's logits are in B1
     }
+    wait_step(v_lo);
+    lds_barrier();
+    // steady intervals v_lo+1 .. v_hi-2: from here, at the start of an even
+    // count of them, S(v-1) is in B0 and S(v) in B1
+    int v = v_lo + 1;
+    if (n_st > 2 && ((n_st - 2) & 1)) {
+      steady(v, B0, B1);
+      ++v;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const v4f t = B0[nt];
+        B0[nt] = B1[nt];
+        B1[nt] = t;
+      }
+    }
+    for (; v + 2 < v_hi; v += 2) {
+      steady(v, B0, B1);
+      steady(v + 1, B1, B0);
+    }
+    // interval v_hi - 1 (when it is not v_lo): check and P.V of v_hi - 2, the last softmax
+    if (v_hi - 1 > v_lo) {
+      check(v_hi - 2, B0);
+      pv_body(v_hi - 2, pv_prep(v_hi - 2, false));
+      soft(v_hi - 1, B1, true);
+      wait_step(v_hi - 1);
+      lds_barrier();
+    }
+    // the last interval: check and P.V of step v_hi - 1, past the stream's end zeroed
+    check(v_hi - 1, B1);
+    pv_body(v_hi - 1, pv_prep(v_hi - 1, (v_hi - 1) * BK + BK > n_keys_t));
   }
 
   // Row sums: each wave's partial over its keys (summed across the column's
@@ -492,7 +579,7 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const float l = rows4_sum(l_part[nt]);
-    if (a == 0) Lx[qcol(nt) * 4 + s] = l;
+    if (a == 0) Mx[qcol(nt) * 4 + s] = l;
   }
   lds_barrier();
   if (s == 0 && a == 0) {
@@ -502,10 +589,11 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
       if (!k.ok) continue;
       const int64_t slot =
           S.slot_base + ((int64_t)k.row * A.n_q_heads + k.head) * S.n_splits + split;
-      const v4f l4 = *reinterpret_cast<const v4f*>(Lx + qcol(nt) * 4);
-      // p was exp2(s*c - (m_run*c - 6)): the split's reference logit in log2
-      // units is m_run*c - 6; a rejected page id poisons it as a NaN
-      const float mref = m_run[nt] == -INFINITY ? -INFINITY : m_run[nt] * cc[nt] - kPScale;
+      const v4f l4 = *reinterpret_cast<const v4f*>(Mx + qcol(nt) * 4);
+      // p was 2^(s*cc - mc): the split's reference logit in log2 units is mc
+      // (minus infinity when the column saw no key); a rejected page id
+      // poisons it as a NaN
+      const float mref = mc[nt] == kNoMax ? -INFINITY : mc[nt];
       A.ws_ml[2 * slot] = bad ? __builtin_nanf("") : mref;
       A.ws_ml[2 * slot + 1] = ((l4[0] + l4[1]) + l4[2]) + l4[3];
     }

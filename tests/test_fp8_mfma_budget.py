@@ -11,12 +11,14 @@ only the extra rounding such a kernel needs:
     3e-2 bound;
   * two terms: x = hi + lo with hi = E4M3(x) and lo = E4M3(x - hi), Q first
     scaled per (row, head) by a power of two that puts max|q| at most 448,
-    P (in (0, 1] after the exact max) scaled by 2^6, as the fp8 verify
-    kernel scales it (a running max that lags the true one by up to 2 in
+    P (in (0, 1] after the exact max) scaled by 2^4, as the fp8 verify
+    kernel scales it (a running max that lags the true one by up to 4 in
     log2 units only raises p, up to 2^8).  Two codes carry 8 significant
-    bits, about bf16's precision: the error is about 1e-3.  Unscaled, the
-    small weights fall into E4M3's subnormal range and the error reaches
-    1e-2 and more.
+    bits, about bf16's precision: the error is 0.7e-3 to 3e-3 (2^6 would
+    give 0.6e-3 to 1.1e-3, at the price of a lag of only 2, which moves
+    some running max of a 96-column tile in about half of all 64-key
+    steps).  Unscaled, the small weights fall into E4M3's subnormal range
+    and the error reaches 1e-2 and more.
 This file pins these measurements."""
 from __future__ import annotations
 
@@ -76,7 +78,7 @@ def _budget(wl, rows):
                 if pm == "one":
                     p = _e4m3(p * 448) / 448
                 elif pm == "two":
-                    p = _two_term(p, 64.0)
+                    p = _two_term(p, 16.0)
                 elif pm == "two-unscaled":
                     p = _two_term(p)
                 per[name].append(p @ Vg / l)
@@ -96,10 +98,10 @@ def test_fp8_products_one_term_exceed_two_terms_fit(ctx, n_rows, rows, seed):
     assert e["q"] > FP8_TOL / 2 and e["p"] > FP8_TOL / 2
     # ... and both together are over it
     assert e["qp"] > FP8_TOL
-    # two E4M3 terms per operand (P scaled by 2^6) keep the error an order of
-    # magnitude below the tolerance; bf16 Q splits exactly
+    # two E4M3 terms per operand (P scaled by 2^4) keep the error about an
+    # order of magnitude below the tolerance; bf16 Q splits exactly
     assert e["q2"] <= 1e-5
-    assert e["p2"] <= 2e-3 and e["q2p2"] <= 2e-3
+    assert e["p2"] <= 4e-3 and e["q2p2"] <= 4e-3
     # without the scale the weights lose their low bits in the subnormals
     assert e["p2u"] > 5 * e["p2"]
 
