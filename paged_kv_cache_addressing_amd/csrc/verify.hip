@@ -52,12 +52,17 @@
 // a half steps to land; the waiting wave then passes the barrier that
 // publishes them (K(v+2) and V(v) are awaited before barrier v).
 //
-// LDS fragment orders (each lane's 16 bytes at lane*16, conflict-free):
-//   K entry b of lane (i, a): dims 64b + 16a .. +15 of key 16s + i; the QK
-//     operand of k-step kk is entries 2kk, 2kk+1, and Q's operand bytes
-//     follow the same dims;
-//   V entry b of lane (d, g): keys 32g + 16b .. +15 of dim d of the tile;
-//     P's operand bytes follow the same keys.
+// LDS fragment orders.  Every DMA instruction reads whole 128-byte lines
+// (8 keys x 128 dims of K, or 16 dims x 64 keys of the V block).  A DMA
+// that gathers 64-byte half lines instead (16 keys at once) streams about
+// 16% slower on this chip.  Each lane's 16 bytes land at lane*16; the lanes
+// take a row's 16-byte pieces in an XOR-swizzled order, so that the operand
+// reads (one piece of 16 keys, or of 32 dims, per instruction) hit every
+// bank once:
+//   K: QK lane (n, a) reads pieces a and 4 + a of key 16s + n (its k-step's
+//     dims 16a.. and 64 + 16a..); Q's operand bytes follow the same dims;
+//   V: P.V lane (d, g) reads pieces 2g and 2g + 1 of dim d's 64 keys (keys
+//     32g .. 32g + 31); P's operand bytes follow the same keys.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -92,11 +97,16 @@ __device__ __forceinline__ v8i join8(v4u x, v4u y) {
 // codes in one dword (byte i for x_i), the lo codes in another.
 __device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, uint32_t& hi,
                                        uint32_t& lo) {
-  int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  // the first conversion of each dword fills its low half; the second, the
+  // high half, so the initial contents do not matter (no zeroing move)
+  int u0, u1;
+  asm("" : "=v"(u0));
+  asm("" : "=v"(u1));
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, u0, false);
   h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
   const v2fe b0 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
   const v2fe b1 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-  int l = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - b0[0], x1 - b0[1], 0, false);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - b0[0], x1 - b0[1], u1, false);
   l = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - b1[0], x3 - b1[1], l, true);
   hi = (uint32_t)h;
   lo = (uint32_t)l;
@@ -112,7 +122,6 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   constexpr int CW = 16 * NTW;               // QK columns per wave
   constexpr int NCOL = 16 * NTG;             // columns per workgroup
   constexpr int KK = D / 128;                // QK k-steps
-  constexpr int KR = D / 64;                 // K entries per key row (64 dims each)
   constexpr int DS = D / 4;                  // P.V dims per SIMD
   constexpr int MTS = DS / 32;               // 32-dim P.V m-tiles per SIMD (2 or 1)
   constexpr int NPV = NCOL / 32;             // 32-column P.V n-tiles per workgroup
@@ -124,11 +133,11 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   constexpr int MXS = NCOL * 4;              // floats of the maxima: [column][SIMD]
   constexpr float kPScale = 4.f;             // P carries a 2^4 scale (log2 units)
   constexpr float kLag = 4.f;                // running max lags by at most this (log2 units)
-  static_assert(4 * KR * 64 == STG && 4 * MTS * 2 * 64 == STG, "a stage is 4 SIMDs' fragments");
+  static_assert(8 * KK * 64 == STG && (D / 16) * 64 == STG, "a stage is 1 KB fragments");
   static_assert(8 * TPW * 64 == STG, "eight waves share a stage's DMAs");
   static_assert(kPage % BK == 0, "a step never straddles two pages");
   static_assert(kPScale + kLag <= 8.f, "p <= 256 fits E4M3");
-  __shared__ v4u lds[(NK + NV) * STG + 2 * PSL + (MXS + 2 * NCOL + 4) / 4];
+  __shared__ v4u lds[(NK + NV) * STG + 2 * PSL + (MXS + 2 * NCOL + 4 + 64) / 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -184,8 +193,12 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   const float c = A.scale_log2;
   // Q^T operands (two E4M3 terms) of this wave's columns, and per column the
   // logit scale c / sigma and the lag threshold in raw logit units.
+  // Q is loaded and split after the first K and V tiles are on their way
+  // (q_operands, called after the prologue's DMAs), so that a workgroup
+  // waits out one memory latency before its first step, not two.
   v8i qh[NTW][KK], ql[NTW][KK];
   float cc[NTW];
+  auto q_operands = [&]() __attribute__((always_inline)) {
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const Col k = col_of(qcol(nt));
@@ -234,6 +247,7 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
                        (int)lw[6], (int)lw[7]};
     }
   }
+  };
 
   v4u* const Kring = lds;
   v4u* const Vring = lds + NK * STG;
@@ -242,15 +256,8 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   float* const Al = Mx + MXS;                                    // rescale factors
   uint32_t* const Anc = reinterpret_cast<uint32_t*>(Al + NCOL);  // ancestor words [column]
   uint8_t* const Fb = reinterpret_cast<uint8_t*>(Anc + NCOL);      // overflow flags [slot][wave]
+  int32_t* const Pid = reinterpret_cast<int32_t*>(Fb + 16);         // page ids of the item
 
-  // Ancestor words of the QK columns' rows (all ones: the causal chain),
-  // read once into LDS: a global load inside the step loop would make the
-  // masked steps wait for every DMA in flight.
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const Col k = col_of(qcol(nt));
-    if (s == 0 && a == 0) Anc[qcol(nt)] = (S.tree_mask && k.ok) ? S.tree_mask[k.row] : 0xFFFFFFFFu;
-  }
   typedef __attribute__((address_space(3))) v4u lds_v4u;
 
   // Page tiles.  The stream's fields stay in registers (TileMap), and the
@@ -263,29 +270,49 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   const int t_last = v_hi > v_lo ? (v_hi - 1) >> 2 : v_lo >> 2;  // last page of the item
   PageTile TK{}, TKprev{};
   int pk = -1;
-  int32_t next_id = 0;
-  bool bad = false;
+  // The item's page ids (up to 64) are copied into LDS in the prologue: a
+  // page switch inside the loop then reads LDS, not the page table.  A
+  // scalar load would hold up the next lgkmcnt wait (the barrier's) for a
+  // trip to memory.  The first page's id is a scalar load (the prologue's
+  // tiles need it before the copy lands); an item of more than 64 pages
+  // reads the rest with scalar loads.
+  const int t0 = v_lo >> 2;
+  auto page_id = [&](int t) -> int32_t {
+    const int i = t - t0;
+    if (map.paged && i < 64) return __builtin_amdgcn_readfirstlane(Pid[i]);
+    return map.id(t);
+  };
   auto page_k = [&](int v) -> const PageTile& {
     const int t = v >> 2;
     if (t != pk) {
-      const int32_t idv = pk < 0 ? map.id(t) : next_id;
-      next_id = map.id(min(t + 1, t_last));
+      const int32_t idv = pk < 0 ? map.id(t) : page_id(t);
       TKprev = TK;
       TK = map.tile(idv);
-      bad |= !TK.ok;
       pk = t;
     }
     return TK;
   };
   auto page_v = [&](int v) -> const PageTile& { return (v >> 2) == pk ? TK : TKprev; };
+  // Each DMA instruction moves one 1 KB fragment of whole 128-byte lines:
+  //   K fragment F = kb * KK + h: keys 8kb .. 8kb+7 of the step, dims
+  //     128h .. 128h+127; lane l takes key l / 8, 16-byte piece
+  //     (l % 8) ^ kswz(l / 8, kb) of the key's 128 bytes;
+  //   V fragment G: dims 16G .. 16G+15 (each a 64-byte row of 64 keys); lane
+  //     l takes dim l / 4, piece (l % 4) ^ vswz(l / 4).
+  // A lane's 16 bytes land at lane*16 in the fragment, so the XOR moves the
+  // pieces of a row apart across the LDS banks: the operand reads below
+  // (16 keys or 32 dims at the same piece) then meet no bank conflict.
+  auto kswz = [](int kl, int kb) { return (kl >> 1) + 4 * (kb & 1); };
+  auto vswz = [](int dl) { return (dl >> 2) & 3; };
   auto dma_k = [&](int v) {
     const PageTile& T = page_k(v);
     const auto rs = tile_rsrc(T.k, kPage * D);
     v4u* dst = Kring + ((v - v_lo) & (NK - 1)) * STG;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int f = wave * TPW + i, sk = f / KR, b = f % KR;  // keys 16sk + n, dims 64b + 16a
-      dma16(rs, (16 * sk + n) * D + 64 * b + 16 * a, (v & 3) * BK * D, dst + f * 64);
+      const int f = wave * TPW + i, kb = f / KK, h = f % KK, kl = lane >> 3;
+      const int piece = (lane & 7) ^ kswz(kl, kb);
+      dma16(rs, (8 * kb + kl) * D + 128 * h + 16 * piece, (v & 3) * BK * D, dst + f * 64);
     }
   };
   auto dma_v = [&](int v) {
@@ -294,20 +321,27 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
     v4u* dst = Vring + ((v - v_lo) & (NV - 1)) * STG;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      // SIMD sv, dim tile mt, half b: keys 32g + 16b .. of dim DS*sv + 32mt + d
-      const int f = wave * TPW + i, sv = f / (2 * MTS), mt = (f >> 1) % MTS, b = f & 1;
-      dma16(rs, (DS * sv + 32 * mt + c32) * 64 + 32 * g32 + 16 * b, (v & 3) * D * 64,
-            dst + f * 64);
+      const int f = wave * TPW + i, dl = lane >> 2;
+      const int piece = (lane & 3) ^ vswz(dl);
+      dma16(rs, (16 * f + dl) * 64 + 16 * piece, (v & 3) * D * 64, dst + f * 64);
     }
   };
+  // Operand read offsets (16-byte entries within a stage).  QK: lane (n, a)
+  // reads key 16s + n, pieces a and 4 + a of k-step kk: fragment
+  // (2s + n / 8) * KK + kk, slot (n % 8) * 8 + (piece ^ kswz).  P.V: lane
+  // (d, g) reads dim DS*s + 32*mt + d, pieces 2g and 2g + 1: fragment
+  // (DS*s + 32*mt + d) / 16, slot (d % 16) * 4 + (piece ^ vswz).  The second
+  // piece's slot is the first's with one bit flipped (4 + a = a ^ 4 and
+  // 2g + 1 = 2g ^ 1 commute with the XOR).
+  const int k_rd = ((2 * s + (n >> 3)) * KK) * 64 + (n & 7) * 8 + (a ^ kswz(n & 7, n >> 3));
+  const int v_rd = ((DS * s + 32 * (MTS == 2 ? hh : 0) + c32) >> 4) * 64 + (c32 & 15) * 4 +
+                   ((2 * g32) ^ vswz(c32 & 15));
 
   // P.V accumulators: n-tile j of this wave is workgroup n-tile n0_w + j;
   // lane (c, grp) holds rows (dims) 8q + 4grp + r of column c at index 4q + r.
   const int mt_w = MTS == 2 ? hh : 0;        // this wave's P.V dim tile
   const int n0_w = MTS == 2 ? 0 : hh * NPW;  // its first P.V n-tile
-  v16f o[NPW];
-#pragma unroll
-  for (int j = 0; j < NPW; ++j) o[j] = v16f{};
+  v16f o[NPW];  // zeroed after the Q operands are built
   // Per column: the exponent offset mc (log2 units, the same in every wave of
   // the column; -FLT_MAX until the column has seen a key), so that
   // p = 2^(s*cc - mc); the row-sum partial; the last step's row-sum terms.
@@ -328,13 +362,12 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   // S(u) = K(u) Q^T for this SIMD's 16 keys, then, in the steps that reach a
   // row's own keys or the stream's end, the mask.
   auto qk = [&](int u, v4f (&Sx)[NTW]) __attribute__((always_inline)) {
-    const lds_v4u* Lk =
-        (const lds_v4u*)(Kring + ((u - v_lo) & (NK - 1)) * STG + s * KR * 64 + lane);
+    const lds_v4u* Lk = (const lds_v4u*)(Kring + ((u - v_lo) & (NK - 1)) * STG);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) Sx[nt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const v8i ka = join8(Lk[(2 * kk) * 64], Lk[(2 * kk + 1) * 64]);
+      const v8i ka = join8(Lk[k_rd + kk * 64], Lk[(k_rd ^ 4) + kk * 64]);
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         Sx[nt] = mfma8_16(ka, qh[nt][kk], Sx[nt]);
@@ -366,6 +399,7 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   // terms into P slot (v & 1), the row-sum terms lp, and (when `flag`) this
   // wave's overflow flag: some logit of its keys above the running max by
   // more than the lag, so that P(v) may not fit the scale.
+  const int p_lane = n * 4 + a;  // dword of a P entry that this lane writes
   auto soft = [&](int v, const v4f (&Sx)[NTW], bool flag) __attribute__((always_inline)) {
     v4u* pd = Pring + ((v - v_lo) & 1) * PSL;
     bool ov = false;
@@ -381,13 +415,15 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
       uint32_t hi, lo;
       split4(p[0], p[1], p[2], p[3], hi, lo);
       // key 16s + 4a + i = 32 gp + 16 bp + 4a + i: dword a of the P.V operand
-      // entry (half bp) of lane (column % 32, gp)
-      const int cl = qcol(nt);
-      const int N = cl >> 5, e = (cl & 31) + 32 * (s >> 1), bp = s & 1;
-      uint32_t* dh = reinterpret_cast<uint32_t*>(pd + ((0 * NPV + N) * 2 + bp) * 64 + e);
-      uint32_t* dl = reinterpret_cast<uint32_t*>(pd + ((1 * NPV + N) * 2 + bp) * 64 + e);
-      dh[a] = hi;
-      dl[a] = lo;
+      // entry (half bp) of lane (column % 32, gp).  The wave's column base
+      // cb = CW hh + 16 nt is a multiple of 16, so column cb + n stays in
+      // 32-column tile cb / 32 at lane (cb % 32) + n: a wave-uniform entry
+      // plus the lane's dword n * 4 + a.
+      const int cb = CW * hh + 16 * nt;
+      const int eu = ((cb >> 5) * 2 + (s & 1)) * 64 + (cb & 31) + 32 * (s >> 1);
+      uint32_t* dh = reinterpret_cast<uint32_t*>(pd + eu) + p_lane;
+      dh[0] = hi;
+      dh[NPV * 2 * 64 * 4] = lo;  // the lo term's entries follow the hi term's
       ov |= fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])) > kPScale + kLag;
     }
     if (flag) {
@@ -441,9 +477,8 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   // P.V of step u (O^T += V(u)^T P(u)^T over its 64 keys for this wave's
   // dims and columns): pv_prep reads the V operand, pv_body multiplies.
   auto pv_prep = [&](int u, bool tail) -> v8i {
-    const lds_v4u* Lv = (const lds_v4u*)(Vring + ((u - v_lo) & (NV - 1)) * STG +
-                                         (s * MTS + mt_w) * 2 * 64 + lane);
-    v4u x0 = Lv[0], x1 = Lv[64];
+    const lds_v4u* Lv = (const lds_v4u*)(Vring + ((u - v_lo) & (NV - 1)) * STG);
+    v4u x0 = Lv[v_rd], x1 = Lv[v_rd ^ 1];
     if (tail) {
       // the stream's last step may run past its last key: those values
       // (unwritten slots, possibly NaN codes) become zeros
@@ -477,17 +512,30 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
     else wait_vmem<0>();
   };
 
+  const int n_st = v_hi - v_lo;
   if (v_hi > v_lo) {
-    // Prologue, in the order the steady state expects: K(v_lo), K(v_lo+1);
-    // then as "step v_lo-2" K(v_lo+2), V(v_lo), and as "step v_lo-1"
-    // K(v_lo+3), V(v_lo+1).
-    const int n_st = v_hi - v_lo;
+    // Prologue DMAs, in the order the steady state expects: K(v_lo),
+    // K(v_lo+1); then as "step v_lo-2" K(v_lo+2), V(v_lo), and as "step
+    // v_lo-1" K(v_lo+3), V(v_lo+1).  All lie in the item's first page.
     dma_k(v_lo);
     if (n_st > 1) dma_k(v_lo + 1);
     if (n_st > 2) dma_k(v_lo + 2);
     dma_v(v_lo);
     if (n_st > 3) dma_k(v_lo + 3);
     if (n_st > 1) dma_v(v_lo + 1);
+  }
+  // Q operands, ancestor words and the page ids, while the first tiles load
+  q_operands();
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) o[j] = v16f{};
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const Col k = col_of(qcol(nt));
+    if (s == 0 && a == 0) Anc[qcol(nt)] = (S.tree_mask && k.ok) ? S.tree_mask[k.row] : 0xFFFFFFFFu;
+  }
+  if (wave == 0 && map.paged) Pid[lane] = t0 + lane <= t_last ? map.pt[t0 + lane] : 0;
+
+  if (v_hi > v_lo) {
     // K(v_lo) and K(v_lo+1) landed: after them at most K(v_lo+2), V(v_lo),
     // K(v_lo+3), V(v_lo+1) remain
     {
@@ -510,8 +558,9 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
     // V(v+2), the check and the P.V of step v-1, the softmax of step v and
     // S(v+1).
     auto steady = [&](int v, v4f (&X)[NTW], v4f (&Y)[NTW]) __attribute__((always_inline)) {
-      check(v - 1, X);
+      // the V operand's reads go out with the flag read, under one wait
       const v8i va = pv_prep(v - 1, false);
+      check(v - 1, X);
       if (v + 4 < v_hi) dma_k(v + 4);
       // the P.V products of step v-1 and the softmax of step v: one
       // branch-free block, each MFMA followed by a share of the VALU work
@@ -572,6 +621,14 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
     check(v_hi - 1, B1);
     pv_body(v_hi - 1, pv_prep(v_hi - 1, (v_hi - 1) * BK + BK > n_keys_t));
   }
+
+  // A rejected page id (out of the pool) anywhere in the item poisons its
+  // partials: checked here, one id per lane, rather than carried through the
+  // step loop.  (The tiles of such pages read page 0 instead.)
+  bool bad_lane = false;
+  if (map.paged && v_hi > v_lo)
+    for (int t = t0 + lane; t <= t_last; t += 64) bad_lane |= (uint32_t)map.pt[t] >= (uint32_t)map.n_pages;
+  const bool bad = __any(bad_lane);
 
   // Row sums: each wave's partial over its keys (summed across the column's
   // four lane groups), then, for every column, the four SIMDs' sums in SIMD
