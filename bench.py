@@ -34,6 +34,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = ["paged_kv_cache_addressing_amd/csrc/decode.hip",
                   "paged_kv_cache_addressing_amd/csrc/prefill.hip",
+                  "paged_kv_cache_addressing_amd/csrc/verify.hip",
                   "paged_kv_cache_addressing_amd/csrc/pa_device.hpp",
                   "paged_kv_cache_addressing_amd/csrc/pa_kargs.hpp"]
 
@@ -64,6 +65,13 @@ def kv_bytes(wl) -> int:
     return sum(st.first_pos + st.n_rows for st in wl.streams) * per_pos
 
 
+def kv_bytes_stream(wl, s) -> int:
+    """KV bytes one decode pass reads for stream s."""
+    esz = 2 if wl.kv_dtype == "bf16" else 1
+    st = wl.streams[s]
+    return (st.first_pos + st.n_rows) * 2 * wl.n_kv_heads * wl.head_dim * esz
+
+
 def attn_flops(wl) -> int:
     """4 * D * Hq flop per visible (row, key) pair (QK^T and PV)."""
     pairs = 0
@@ -90,11 +98,22 @@ class EventTimer:
         self.e.record()
         self.pairs.append((self.s, self.e))
 
-    def mean_ms(self) -> float:
+    def times_ms(self) -> list:
         import torch
         torch.cuda.synchronize()
-        ts = [s.elapsed_time(e) for s, e in self.pairs]
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+    def mean_ms(self) -> float:
+        ts = self.times_ms()
         return sum(ts) / len(ts)
+
+    def stats(self) -> dict:
+        """Mean, median and min of the recorded durations (ms)."""
+        ts = sorted(self.times_ms())
+        n = len(ts)
+        med = ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2])
+        return {"mean": round(sum(ts) / n, 5), "median": round(med, 5), "min": round(ts[0], 5),
+                "n": n}
 
 
 def traffic_for(kernel: str, workload: str):
@@ -134,7 +153,7 @@ def setup_decode(wl):
     return res, ws, out, new_k, new_v, store
 
 
-def run_decode(wl, steps, warmup, with_store=True):
+def run_decode(wl, steps, warmup, with_store=True, aa=False):
     """Time `steps` decode steps (store, partials, merge).  Inside the timed
     region only the partial kernel is bracketed by events (the roofline
     kernel); the store and merge durations come from a short pass after it,
@@ -179,7 +198,21 @@ def run_decode(wl, steps, warmup, with_store=True):
         partials()
         with t_merge:
             merge()
-    r = {"ms_per_step": wall_ms, "partial_ms": t_part.mean_ms(), "merge_ms": t_merge.mean_ms()}
+    # A/A: a second arm of the same steps, to show the run-to-run spread
+    t_arm2 = EventTimer()
+    if aa:
+        for _ in range(steps):
+            if with_store:
+                pa.write_kv(res.cache, store, nk, nv)
+            with t_arm2:
+                partials()
+            merge()
+    r = {"ms_per_step": wall_ms, "partial_ms": t_part.mean_ms(), "merge_ms": t_merge.mean_ms(),
+         "partial_stats": t_part.stats()}
+    if aa:
+        a1, a2 = r["partial_ms"], t_arm2.mean_ms()
+        r["aa"] = {"arm1_partial_ms": round(a1, 5), "arm2_partial_ms": round(a2, 5),
+                   "spread": round(abs(a1 - a2) / a1, 5)}
     if with_store:
         r["store_ms"] = t_store.mean_ms()
     return r, res, out
@@ -204,7 +237,34 @@ def run_prefill(wl, steps, warmup):
             pa.paged_attn_prefill(res.cache, res.streams, res.q, out=out, sm_scale=res.sm_scale)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    return {"ms_per_step": wall_ms, "prefill_ms": t.mean_ms()}
+    return {"ms_per_step": wall_ms, "prefill_ms": t.mean_ms(), "prefill_stats": t.stats()}
+
+
+def run_latency(wl, calls=200, warmup=20):
+    """Latency of one decode call (partials + merge) on a small workload: HIP
+    events around each call, median and min over `calls` calls."""
+    import torch
+
+    import paged_kv_cache_addressing_amd as pa
+    from paged_kv_cache_addressing_amd.resident import upload
+    res = upload(wl)
+    ws = pa.decode_workspace(res.cache, res.streams, wl.n_q_heads, wl.split_keys)
+    out = torch.empty_like(res.q)
+
+    def call():
+        pa.paged_attn_decode(res.cache, res.streams, res.q, out=out, sm_scale=res.sm_scale,
+                             split_keys=res.split_keys, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t = EventTimer()
+    for _ in range(calls):
+        with t:
+            call()
+    st = t.stats()
+    return {"workload": wl.name, "call": "paged_attn_decode (partials + merge)",
+            "median_us": round(st["median"] * 1e3, 2), "min_us": round(st["min"] * 1e3, 2),
+            "mean_us": round(st["mean"] * 1e3, 2), "calls": calls}
 
 
 # ----------------------------------------------------------------------------- oracle baseline
@@ -222,7 +282,7 @@ def cpu_baseline(wl, min_s: float = 10.0):
     def bits16(t):
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = oracle_threads()
     hkv, d = wl.n_kv_heads, wl.head_dim
     ps = hkv * 256 * d
     kp = np.zeros((wl.n_pages, hkv, 256, d), np.uint16)
@@ -246,7 +306,102 @@ def cpu_baseline(wl, min_s: float = 10.0):
             "kind": "oracle",
             "sample": f"{n_calls} stream passes over the decode batch's 8 streams (whole "
                       f"65,536-position context, all 24 q heads, float64 gather+softmax, "
-                      f"{threads} threads over (row, q head)), {spent:.1f} s"}
+                      f"{threads} threads over (row, q head)), {spent:.1f} s",
+            "host": host_cpus()}
+
+
+def oracle_threads() -> int:
+    """Threads the oracle runs on: the process's CPUs, at most 16 (one GPU's
+    share of the host on the boxes this runs on)."""
+    return min(16, len(os.sched_getaffinity(0)))
+
+
+def host_cpus() -> dict:
+    """The host's processor counts, apart from the threads the oracle uses:
+    logical CPUs (what nproc and std::thread::hardware_concurrency report)
+    and the CPUs this process may run on."""
+    return {"logical_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "oracle_threads": oracle_threads(),
+            "cap": "the oracle uses at most 16 threads, one GPU's share of the host"}
+
+
+def oracle_stream_time(wl, s, rows, threads, min_s):
+    """Seconds per oracle call over rows `rows` of stream s (a contiguous copy of
+    the stream's cache, built once), repeated until min_s seconds are spent."""
+    import numpy as np
+
+    import torch
+
+    import oracle
+
+    def bits16(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    st = wl.streams[s]
+    dt = oracle.DTYPE_BF16 if wl.kv_dtype == "bf16" else oracle.DTYPE_E4M3
+    npd = np.uint16 if wl.kv_dtype == "bf16" else np.uint8
+    k = np.zeros((st.ctx_len, wl.n_kv_heads, wl.head_dim), npd)
+    v = np.zeros_like(k)
+    oracle.store(k, v, dt, bits16(wl.k_rows[s]), bits16(wl.v_rows[s]), 0, k_scale=wl.k_scale,
+                 v_scale=wl.v_scale, n_threads=threads)
+    q = bits16(wl.q[st.row_offset:st.row_offset + st.n_rows])
+    sel = np.array(rows, np.int32)
+    n, spent = 0, 0.0
+    while n == 0 or spent < min_s:
+        t0 = time.perf_counter()
+        oracle.attention(k, v, dt, q, st.first_pos, wl.n_kv_heads, st.ctx_len, rows=sel,
+                         sm_scale=wl.sm_scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                         n_threads=threads)
+        spent += time.perf_counter() - t0
+        n += 1
+    return spent / n, n, spent
+
+
+def cpu_baseline_others(wls: dict, min_s: float = 2.0):
+    """Oracle timings on the other workloads (`wls`: config name -> workload,
+    built by the GPU legs), each a bounded sample."""
+    import workloads
+    out = {}
+    thr = oracle_threads()
+    for name in ("config1", "config2"):
+        wl = wls.get(name) or getattr(workloads, name)()
+        st = wl.streams[0]
+        t, n, spent = oracle_stream_time(wl, 0, [0], 1, min_s)
+        nb = kv_bytes_stream(wl, 0)
+        out[f"{name}_1thread"] = {
+            "value": round(nb / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "latency_ms": round(t * 1e3, 3),
+            "sample": f"stream 0 of {wl.name} (1 row, {st.ctx_len} keys, all {wl.n_q_heads} q "
+                      f"heads), {n} calls in {spent:.1f} s on 1 thread"}
+        log(f"oracle {name} 1 thread: {out[name + '_1thread']['value']} GB/s")
+    wl = wls.get("config4") or workloads.config4()
+    st = wl.streams[0]
+    rows = [0, 1365, 2730, 4095]
+    t, n, spent = oracle_stream_time(wl, 0, rows, thr, min_s)
+    pairs = sum(st.first_pos + r + 1 for r in rows)
+    fl = 4 * wl.head_dim * wl.n_q_heads * pairs
+    out["config4_sampled"] = {
+        "value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": thr,
+        "projected_full_s": round(t * attn_flops(wl) / fl, 1),
+        "sample": f"rows {rows} of the 4,096-row prefill ({pairs} row-key pairs, all 24 q heads), "
+                  f"{n} calls in {spent:.1f} s; projected_full_s scales by the workload's flop"}
+    log(f"oracle config4 sampled: {out['config4_sampled']['value']} TFLOP/s")
+    wl = wls.get("config5") or workloads.config5()
+    st = wl.streams[0]
+    rows = [0, 15]
+    t, n, spent = oracle_stream_time(wl, 0, rows, thr, min_s)
+    total_rows = sum(x.n_rows for x in wl.streams)
+    per_row = t / len(rows)
+    # every row re-reads its stream's keys in the oracle: a row of stream 0
+    # stands for a row of average context
+    mean_ctx = sum(x.ctx_len for x in wl.streams) / len(wl.streams)
+    proj = per_row * total_rows * mean_ctx / st.ctx_len
+    out["config5_sampled"] = {
+        "value": round(kv_bytes(wl) / proj / 1e9, 4), "unit": "GB/s", "cores": thr,
+        "projected_full_s": round(proj, 1),
+        "sample": f"rows {rows} of stream 0 ({st.ctx_len} keys, fp8, all 24 q heads), {n} calls "
+                  f"in {spent:.1f} s; scaled to all {total_rows} rows at the batch's mean context"}
+    log(f"oracle config5 sampled: {out['config5_sampled']['value']} GB/s")
+    return out
 
 
 # ----------------------------------------------------------------------------- main
@@ -320,7 +475,7 @@ def main():
 
     wl = workloads.config2()
     log(f"decode {wl.name}: uploading")
-    r, res, out = run_decode(wl, args.steps, args.warmup)
+    r, res, out = run_decode(wl, args.steps, args.warmup, aa=True)
     nbytes = kv_bytes(wl)
     value = nbytes / (r["ms_per_step"] * 1e-3) / 1e9
     achieved = nbytes / (r["partial_ms"] * 1e-3) / 1e9
@@ -351,14 +506,18 @@ def main():
                      "traffic": traffic_for("decode_partial_kernel<bf16,256>", "config2"),
                      "kernel_ms": round(r["partial_ms"], 5),
                      "algorithmic_bytes": nbytes},
-        "kernel_ms": {k: round(v, 5) for k, v in r.items()},
+        "kernel_ms": {k: round(v, 5) for k, v in r.items() if isinstance(v, float)},
+        "partial_ms_stats": r["partial_stats"],
+        "aa": r["aa"],
     }
     del res, out
     torch.cuda.empty_cache()
 
+    kept = {"config2": wl}  # host-side workloads reused by the oracle timings
     if not args.no_secondary:
         sec = {}
         wl4 = workloads.config4()
+        kept["config4"] = wl4
         log(f"prefill {wl4.name}")
         # the GPU idles while the workload is generated on the host; ten
         # untimed launches (~30 ms) let the clock settle before timing
@@ -370,8 +529,8 @@ def main():
                           "kernel": "prefill_kernel<bf16,256>", "kernel_ms": round(p["prefill_ms"], 4),
                           "flop": fl, "tflops": round(tf, 2), "peak_tflops": BF16_PEAK_TFLOPS,
                           "frac": round(tf / BF16_PEAK_TFLOPS, 4), "bound": "mfma",
+                          "kernel_ms_stats": p["prefill_stats"],
                           "traffic": traffic_for("prefill_kernel<bf16,256>", "config4")}
-        del wl4
         for name, fn, store in (("decode_fp8_mixed", workloads.config3, True),
                                 ("verify_fp8", workloads.config5, False)):
             w = fn()
@@ -386,20 +545,30 @@ def main():
                          "kv_gbs_step": round(nb / (rr["ms_per_step"] * 1e-3) / 1e9, 2),
                          "frac_hbm_partial": round(nb / (rr["partial_ms"] * 1e-3) / 1e9 /
                                                    HBM_PEAK_GBS, 4),
-                         "tflops_partial": round(fl / (rr["partial_ms"] * 1e-3) / 1e12, 2)}
+                         "frac_hbm_partial_merge": round(nb / ((rr["partial_ms"] + rr["merge_ms"])
+                                                               * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "tflops_partial": round(fl / (rr["partial_ms"] * 1e-3) / 1e12, 2),
+                         "partial_ms_stats": rr["partial_stats"]}
             if name == "verify_fp8":
-                sec[name]["kernel"] = "prefill_kernel<fp8,256> split"
-                sec[name]["traffic"] = traffic_for("prefill_kernel<fp8,256> split", "config5")
+                sec[name]["kernel"] = "verify_kernel<256>"
+                sec[name]["traffic"] = traffic_for("verify_kernel<256>", "config5")
             else:
                 sec[name]["kernel"] = "decode_partial_kernel<fp8,256>"
                 sec[name]["traffic"] = traffic_for("decode_partial_kernel<fp8,256>", "config3")
+            if name == "verify_fp8":
+                kept["config5"] = w
             del w, res, out
             torch.cuda.empty_cache()
+        w1 = workloads.config1()
+        log(f"latency {w1.name}")
+        sec["config1_latency"] = run_latency(w1)
+        kept["config1"] = w1
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(wl)
+        line["cpu_baseline"]["others"] = cpu_baseline_others(kept)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
