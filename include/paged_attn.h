@@ -192,8 +192,9 @@ PA_API int32_t page_pool_free_count(const pa_page_pool *pool);
  * A page is page_stride contiguous elements of K (and of V) starting at
  * element page*page_stride: every kv head of it, and, when the pool holds
  * several layers per page (a layer's view is k_pages/v_pages advanced by
- * its block and the same page_stride, TensorFold pull request #2011,
- * "Checklist": the layer block lblk inside a page), every layer.
+ * its block and the same page_stride: the layer block inside a page of
+ * TensorFold pull request #2011, review section "Is paged output the same
+ * as windowed output?", the bullet on the decode tiles), every layer.
  * page_stride * element size must be a multiple of 16 bytes.  Page ids are
  * host arrays of n entries, each in [0, n_pages).
  *
@@ -201,8 +202,9 @@ PA_API int32_t page_pool_free_count(const pa_page_pool *pool);
  * every i, enqueued on hip_stream.  Destinations must be distinct and no
  * destination may be a source of the same call (PA_ERANGE otherwise).
  *
- * page_save / page_restore: copies between pages and host memory (pull
- * request #2011 review: save and restore make one 2D copy per page).  Page
+ * page_save / page_restore: copies between pages and host memory, one
+ * contiguous block per page (TensorFold pull request #2011, the author's
+ * A/A comment, its list of three local fixes).  Page
  * ids[i] occupies bytes [i*P, (i+1)*P) of host_k and of host_v, P =
  * page_stride * element size; host memory should be pinned for the copies to
  * run asynchronously on hip_stream.  The caller synchronises before reading
@@ -333,7 +335,16 @@ PA_API int paged_attn_decode_plan(const pa_stream *streams, int32_t n_streams, i
  * covers a tile of a stream's rows for some q heads of one kv head (tiles
  * never span streams); a row's bytes do not depend on which other rows
  * share its tile, so any slicing of a stream's rows into calls gives the
- * same bytes as one call. */
+ * same bytes as one call.
+ *
+ * Finite inputs: this kernel (also the one behind the partials of bf16
+ * decode streams with more than a few rows) is built without NaN semantics.
+ * Q, the scales, and K and V at every key a row sees must be finite; a NaN
+ * or infinity there leaves that row's output unspecified (not necessarily
+ * NaN).  Keys a row does not see, and slots past the stream's context, may
+ * hold anything, NaN codes included: they are replaced by selects before
+ * any arithmetic.  A rejected page id still poisons its rows with NaN bit
+ * patterns (written as integers). */
 PA_API int paged_attn_prefill(const pa_kv_cache *cache, const pa_stream *streams, int32_t n_streams,
                        const void *q, void *out, int32_t n_q_heads, float sm_scale,
                        void *hip_stream);
