@@ -385,12 +385,22 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs A) {
   const int ns = S.n_splits;
   const int64_t slot0 = S.slot_base + ((int64_t)r * A.n_q_heads + h) * ns;
   const float* ml = A.ws_ml + 2 * slot0;
+  const float* op = A.ws_o + slot0 * D + t;
+
+  // The first JB splits' o_j go out with the (m_j, l_j) loads: they do not
+  // depend on the maximum, so a call of up to JB splits (every stream up to
+  // 16 x 4,096 keys) waits for memory once.
+  float o0[JB];
+#pragma unroll
+  for (int u = 0; u < JB; ++u) o0[u] = u < ns ? op[(int64_t)u * D] : 0.f;
+  const float m_t = t < ns ? ml[2 * t] : -INFINITY;
+  const float l_t = t < ns ? ml[2 * t + 1] : 0.f;
 
   // M = max_j m_j over the whole block (max is exact in any order); a NaN m
   // marks a partial computed from a rejected page id.
-  float mx = -INFINITY;
-  bool bad = false;
-  for (int j = t; j < ns; j += NT) {
+  float mx = m_t;
+  bool bad = m_t != m_t;
+  for (int j = t + NT; j < ns; j += NT) {
     const float m = ml[2 * j];
     bad |= m != m;
     mx = fmaxf(mx, m);
@@ -412,20 +422,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs A) {
   }
 
   float num = 0.f, den = 0.f;
-  const float* op = A.ws_o + slot0 * D + t;
   for (int j0 = 0; j0 < ns; j0 += MB) {
     const int nj = min(MB, ns - j0);
     __syncthreads();  // the previous run's weights are consumed
     if (t < nj) {
-      const float m = ml[2 * (j0 + t)];
+      const float m = j0 == 0 ? m_t : ml[2 * (j0 + t)];
       sh_w[t] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      sh_l[t] = ml[2 * (j0 + t) + 1];
+      sh_l[t] = j0 == 0 ? l_t : ml[2 * (j0 + t) + 1];
     }
     __syncthreads();
     for (int jb = 0; jb < nj; jb += JB) {
       float ob[JB];
+      if (j0 == 0 && jb == 0) {
 #pragma unroll
-      for (int u = 0; u < JB; ++u) ob[u] = jb + u < nj ? op[(int64_t)(j0 + jb + u) * D] : 0.f;
+        for (int u = 0; u < JB; ++u) ob[u] = o0[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < JB; ++u) ob[u] = jb + u < nj ? op[(int64_t)(j0 + jb + u) * D] : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < JB; ++u) {
         if (jb + u >= nj) break;
