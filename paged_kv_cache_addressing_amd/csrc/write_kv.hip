@@ -30,13 +30,17 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const WriteArgs A) {
   const StreamArg& S = A.s[si];
   const int r = row - S.row_begin;
   const int pos = S.first_pos + r;
+  // The new row's values do not depend on the page: their loads go out
+  // before the page-table read, so the two latencies overlap.  The grid
+  // gives one thread per dim (blockDim.x == D).
+  const int d = threadIdx.x;
+  const int64_t src = ((int64_t)(S.row_offset + r) * A.cache.n_kv_heads + g) * D;
+  const uint16_t kx = A.k_new[src + d];
+  const uint16_t vx = A.v_new[src + d];
   const PageTile T = page_tile<D, ESZ>(S, A.cache, pos / kPage, g);
   if (!T.ok) return;
   const int j = pos % kPage;
-  const int64_t src = ((int64_t)(S.row_offset + r) * A.cache.n_kv_heads + g) * D;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    const uint16_t kx = A.k_new[src + d];
-    const uint16_t vx = A.v_new[src + d];
+  {
     uint8_t* kd = T.k + ((int64_t)j * D + d) * ESZ;
     uint8_t* vd = T.v + (int64_t)v_off<D, ESZ>(j, d) * ESZ;
     if (KV) {
