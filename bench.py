@@ -280,12 +280,55 @@ def run_decode(wl, steps, warmup, with_store=True, aa=False):
     r = {"ms_per_step": wall_ms, "partial_ms": t_part.mean_ms(), "merge_ms": t_merge.mean_ms(),
          "partial_stats": t_part.stats()}
     if aa:
+        r["hbm_probe"] = probe_abba(partials, kv_bytes(wl))
+    if aa:
         a1, a2 = r["partial_ms"], t_arm2.mean_ms()
         r["aa"] = {"arm1_partial_ms": round(a1, 5), "arm2_partial_ms": round(a2, 5),
                    "spread": round(abs(a1 - a2) / a1, 5)}
     if with_store:
         r["store_ms"] = t_store.mean_ms()
     return r, res, out
+
+
+PROBE_BYTES = 8 << 30  # larger runs read faster: 6.25 / 6.21 / 6.44 / 6.63 TB/s at 1 / 2 / 4 / 8 GiB
+
+
+def probe_abba(arm_a, a_bytes: int, launches: int = 10, rounds: int = 3) -> dict:
+    """ABBA rounds of arm A (the decode partial kernel) against arm B, the
+    library's plain streaming read of an 8 GiB buffer (pa_hbm_read_probe):
+    the box's achievable read rate, measured between the same launches."""
+    import torch
+
+    import paged_kv_cache_addressing_amd as pa
+    buf = torch.zeros(PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ta, tb = EventTimer(2 * rounds * launches), EventTimer(2 * rounds * launches)
+
+    def arm(t, f):
+        for _ in range(launches):
+            with t:
+                f()
+
+    def probe():
+        pa.hbm_read_probe(buf, sink)
+    for _ in range(3):
+        probe()
+    for _ in range(rounds):
+        arm(ta, arm_a)
+        arm(tb, probe)
+        arm(tb, probe)
+        arm(ta, arm_a)
+    sa, sb = ta.stats(), tb.stats()
+    del buf
+    probe_gbs = PROBE_BYTES / (sb["median"] * 1e-3) / 1e9
+    a_gbs = a_bytes / (sa["median"] * 1e-3) / 1e9
+    return {"probe": "pa_hbm_read_probe over 8 GiB (one contiguous run per workgroup, "
+                     "1,024 x 512 threads, 32 KiB steps, 4 steps of nontemporal loads in "
+                     "flight)", "rounds": f"ABBA x{rounds}, {launches} launches an arm",
+            "probe_gbs_median": round(probe_gbs, 1),
+            "probe_gbs_max": round(PROBE_BYTES / (sb["min"] * 1e-3) / 1e9, 1),
+            "partial_gbs_median": round(a_gbs, 1),
+            "partial_over_probe": round(a_gbs / probe_gbs, 4)}
 
 
 # ----------------------------------------------------------------------------- prefill
@@ -579,6 +622,7 @@ def main():
         "kernel_ms": {k: round(v, 5) for k, v in r.items() if isinstance(v, float)},
         "partial_ms_stats": r["partial_stats"],
         "aa": r["aa"],
+        "hbm_probe": r["hbm_probe"],
     }
     del res, out
     torch.cuda.empty_cache()

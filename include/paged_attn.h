@@ -146,6 +146,18 @@ PA_API const char *pa_status_string(int status);
 /* Library ABI version: (major << 16) | minor. */
 PA_API int pa_version(void);
 
+/* A plain streaming read of `bytes` of device memory at `buf`, for
+ * measuring the device's achievable HBM read rate beside the attention
+ * kernels (the pages time their arms against such a reference, interleaved:
+ * pull request #2011, the author's A/A comment).  Not part of attention.
+ * buf: device, 16-byte aligned; bytes: a positive multiple of 16; every
+ * 16-byte chunk is read once with nontemporal loads.  sink: device, one
+ * uint32 that the kernel XORs a fold of the data into (so that no load is
+ * dead); its value carries no meaning.  Enqueued on hip_stream (null: the
+ * null stream); PA_EINVAL on a bad argument, PA_EDEVICE if the launch
+ * fails. */
+PA_API int pa_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *hip_stream);
+
 /* ---------------------------------------------------------------- page pool
  * Host-side bookkeeping of which page ids are free (pull request #2011,
  * "Memory admission").  The pool's device memory is the caller's.  A pool

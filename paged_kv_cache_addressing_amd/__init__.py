@@ -39,7 +39,7 @@ EXPORTS = ["pa_status_string", "pa_version", "page_pool_create", "page_pool_dest
            "page_pool_refcount", "page_copy", "page_save", "page_restore", "write_kv",
            "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_partials",
            "paged_attn_decode_merge", "paged_attn_decode_plan", "paged_attn_prefill",
-           "paged_attn_decode_noalloc"]
+           "paged_attn_decode_noalloc", "pa_hbm_read_probe"]
 
 
 class PagedAttnError(RuntimeError):
@@ -123,6 +123,8 @@ def lib():
         L.paged_attn_decode_noalloc.restype = C.c_int
         L.paged_attn_decode_noalloc.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream),
                                                 i32, P, P, i32, f32, i32, P]
+        L.pa_hbm_read_probe.restype = C.c_int
+        L.pa_hbm_read_probe.argtypes = [P, sz, P, P]
         L.paged_attn_prefill.restype = C.c_int
         L.paged_attn_prefill.argtypes = [C.POINTER(pa_kv_cache), C.POINTER(pa_stream), i32, P, P,
                                          i32, f32, P]
@@ -487,6 +489,18 @@ def paged_attn_decode_noalloc(cache: KVCache, streams, q, out, sm_scale: float |
                                            float(sm_scale), int(split_keys),
                                            _hip_stream(stream)), "paged_attn_decode_noalloc")
     return out
+
+
+def hbm_read_probe(buf, sink, stream=None) -> None:
+    """Stream-read the whole of device tensor buf (its bytes a multiple of 16)
+    and fold it into sink (a one-element int32/uint32 device tensor): the
+    reference read rate the attention kernels are measured against."""
+    _v.on_gpu([("buf", buf), ("sink", sink)])
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_contiguous() or sink.numel() < 1 or sink.element_size() != 4:
+        raise ValueError("hbm_read_probe: buf must be contiguous and sink one 32-bit element")
+    _check(lib().pa_hbm_read_probe(_ptr(buf), nbytes, _ptr(sink), _hip_stream(stream)),
+           "pa_hbm_read_probe")
 
 
 def decode_workspace(cache: KVCache, streams, n_q_heads: int,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpaged_attn.so")
 SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "write_kv.hip", "pages.hip", "noalloc.hip",
-           "verify.hip"]
+           "verify.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

@@ -241,7 +241,16 @@ const char* pa_status_string(int status) {
   }
 }
 
-int pa_version(void) { return (1 << 16) | 1; }
+int pa_version(void) { return (1 << 16) | 2; }
+
+int pa_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || ((uintptr_t)buf & 15) ||
+      bytes > (size_t)INT64_MAX)
+    return PA_EINVAL;
+  return pa::launch_hbm_read_probe(buf, (int64_t)bytes, sink, (hipStream_t)hip_stream) == 0
+             ? PA_OK
+             : PA_EDEVICE;
+}
 
 int page_pool_create(int32_t n_pages, pa_page_pool** out) {
   if (!out || n_pages < 1) return PA_EINVAL;

@@ -26,6 +26,9 @@ int verify_wg_columns(int head_dim);
 int launch_verify(const PrefillArgs& A, int head_dim, hipStream_t st);
 int launch_write_kv(const WriteArgs& A, int kv_dtype, int head_dim, hipStream_t st);
 int launch_page_copy(const PageCopyArgs& A, hipStream_t st);
+// Streaming read of bytes (a positive multiple of 16) at buf (16-byte
+// aligned), folded into *sink.
+int launch_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t st);
 
 // Bytes of the fixed device scratch behind paged_attn_decode_noalloc.
 constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;

@@ -529,3 +529,21 @@ def test_context_past_the_stored_rows_control_reads_poison():
     over = pa.Stream(st.ctx_len + 1, 1, st.row_offset, st.first_pos + 1,
                      page_table=st.page_table, layout=st.layout)
     assert torch.isnan(decode(res, streams=[over]).float()).any()
+
+
+def test_hbm_read_probe_reads_every_chunk_once():
+    """The read probe folds every 16-byte chunk into its sink exactly once:
+    its sink equals the XOR of all 32-bit words of the buffer (a chunk read
+    twice would cancel out, a chunk skipped would be missing), for a size
+    whose workgroup runs end in part of a step and leave a remainder past the
+    last run."""
+    g = torch.Generator().manual_seed(77)
+    nbytes = 16 * (1024 * 2048 * 3 + 1024 * 700 + 33)
+    host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g)
+    buf = host.cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pa.hbm_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(want)
+

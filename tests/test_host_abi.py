@@ -37,6 +37,15 @@ def test_library_exports_every_declared_symbol():
     assert pa.lib().pa_version() >> 16 == 1
 
 
+def test_hbm_read_probe_validation():
+    L = pa.lib()
+    sink = C.c_void_p(FAKE)
+    for buf, nbytes, snk in ((None, 1024, sink), (C.c_void_p(FAKE), 1024, None),
+                             (C.c_void_p(FAKE), 0, sink), (C.c_void_p(FAKE), 1000, sink),
+                             (C.c_void_p(FAKE + 8), 1024, sink)):
+        assert L.pa_hbm_read_probe(buf, nbytes, snk, None) == pa.PA_EINVAL
+
+
 def test_every_kernel_launch_stub_is_defined():
     """Each kernel's host-side launch stub is defined in the library (a stub
     the host pass failed to emit would only show as a load error)."""
