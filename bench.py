@@ -290,6 +290,7 @@ def run_decode(wl, steps, warmup, with_store=True, aa=False):
     return r, res, out
 
 
+SETTLE_WARMUP = 100  # untimed steps before the secondary decode workloads are timed
 PROBE_BYTES = 8 << 30  # larger runs read faster: 6.25 / 6.21 / 6.44 / 6.63 TB/s at 1 / 2 / 4 / 8 GiB
 
 
@@ -649,7 +650,13 @@ def main():
                                 ("verify_fp8", workloads.config5, False)):
             w = fn()
             log(f"{name} {w.name}")
-            rr, res, out = run_decode(w, args.steps, args.warmup, with_store=store)
+            # The clock needs tens of launches to settle after the host-side
+            # workload generation: launch by launch, the verify batch ran
+            # 0.51 ms cold, 0.64-0.70 ms at launches 4-10 and 0.50-0.51 ms
+            # from about the 50th on.  The timed launches follow SETTLE_WARMUP
+            # untimed steps.
+            rr, res, out = run_decode(w, args.steps, max(args.warmup, SETTLE_WARMUP),
+                                      with_store=store)
             nb = kv_bytes(w)
             fl = attn_flops(w)
             sec[name] = {"workload": w.name, "kv_bytes": nb,
