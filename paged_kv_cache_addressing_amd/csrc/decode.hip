@@ -362,95 +362,83 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
 
 // out[row][h] = v_scale * sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j, in
 // split order j = 0, 1, ...; a wholly masked split (m_j = -inf) weighs 0.
-// One block per (row, q head), thread d owning dim d.  M is reduced once for
-// the block; then, for each run of up to MB splits, the weights 2^(m_j - M)
-// and l_j go to LDS and every thread streams its dim of o_j, JB splits of
-// loads in flight at a time.  All sums run in split order, so the result
-// does not depend on how the splits are batched.
+// One wave per (row, q head), lane l owning dims DV*l .. DV*l+DV-1 (16-byte
+// loads at D = 256).  Lane j holds the weight 2^(m_j - M) and l_j of split
+// j of the current run of 64; every lane reads them with readlane, so no
+// value goes through LDS and there is no barrier.  The first JB splits' o_j
+// go out with the (m_j, l_j) loads.  All sums run in split order, so the
+// result does not depend on how the splits are batched.
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs A) {
-  constexpr int NT = D;    // threads per block
-  constexpr int MB = NT;   // splits per LDS run
-  constexpr int JB = 16;   // o_j loads in flight per thread
-  __shared__ float sh_w[MB];
-  __shared__ float sh_l[MB];
-  __shared__ float sh_red[NT / 64];
-  __shared__ int sh_bad[NT / 64];
+__global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs A) {
+  constexpr int DV = D / 64;  // dims per lane
+  constexpr int JB = 16;      // splits of o_j loads in flight
+  typedef float vdf __attribute__((ext_vector_type(DV)));
   const int row = blockIdx.x;
   const int h = blockIdx.y;
-  const int t = threadIdx.x;
+  const int lane = threadIdx.x;
   const int si = find_stream<1>(A.s, A.n_streams, row);
   const StreamArg& S = A.s[si];
   const int r = row - S.row_begin;
   const int ns = S.n_splits;
   const int64_t slot0 = S.slot_base + ((int64_t)r * A.n_q_heads + h) * ns;
   const float* ml = A.ws_ml + 2 * slot0;
-  const float* op = A.ws_o + slot0 * D + t;
+  const vdf* op = reinterpret_cast<const vdf*>(A.ws_o + slot0 * D) + lane;
 
-  // The first JB splits' o_j go out with the (m_j, l_j) loads: they do not
-  // depend on the maximum, so a call of up to JB splits (every stream up to
-  // 16 x 4,096 keys) waits for memory once.
-  float o0[JB];
+  vdf o0[JB];
 #pragma unroll
-  for (int u = 0; u < JB; ++u) o0[u] = u < ns ? op[(int64_t)u * D] : 0.f;
-  const float m_t = t < ns ? ml[2 * t] : -INFINITY;
-  const float l_t = t < ns ? ml[2 * t + 1] : 0.f;
+  for (int u = 0; u < JB; ++u) o0[u] = u < ns ? op[(int64_t)u * (D / DV)] : vdf{};
+  const float m_t = lane < ns ? ml[2 * lane] : -INFINITY;
+  const float l_t = lane < ns ? ml[2 * lane + 1] : 0.f;
 
-  // M = max_j m_j over the whole block (max is exact in any order); a NaN m
-  // marks a partial computed from a rejected page id.
+  // M = max_j m_j (exact in any order); a NaN m marks a rejected page id.
   float mx = m_t;
   bool bad = m_t != m_t;
-  for (int j = t + NT; j < ns; j += NT) {
+  for (int j = lane + 64; j < ns; j += 64) {
     const float m = ml[2 * j];
     bad |= m != m;
     mx = fmaxf(mx, m);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  const bool wbad = __any(bad);
-  if ((t & 63) == 0) {
-    sh_red[t >> 6] = mx;
-    sh_bad[t >> 6] = wbad ? 1 : 0;
-  }
-  __syncthreads();
-  float M = sh_red[0];
-  bool any_bad = sh_bad[0] != 0;
-#pragma unroll
-  for (int w = 1; w < NT / 64; ++w) {
-    M = fmaxf(M, sh_red[w]);
-    any_bad |= sh_bad[w] != 0;
-  }
+  const bool any_bad = __any(bad);
+  const float M = mx;
 
-  float num = 0.f, den = 0.f;
-  for (int j0 = 0; j0 < ns; j0 += MB) {
-    const int nj = min(MB, ns - j0);
-    __syncthreads();  // the previous run's weights are consumed
-    if (t < nj) {
-      const float m = j0 == 0 ? m_t : ml[2 * (j0 + t)];
-      sh_w[t] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      sh_l[t] = j0 == 0 ? l_t : ml[2 * (j0 + t) + 1];
+  vdf num = vdf{};
+  float den = 0.f;
+  for (int j0 = 0; j0 < ns; j0 += 64) {
+    const int nj = min(64, ns - j0);
+    float wj = 0.f, lj = 0.f;
+    if (lane < nj) {
+      const float m = j0 == 0 ? m_t : ml[2 * (j0 + lane)];
+      wj = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      lj = j0 == 0 ? l_t : ml[2 * (j0 + lane) + 1];
     }
-    __syncthreads();
     for (int jb = 0; jb < nj; jb += JB) {
-      float ob[JB];
+      vdf ob[JB];
       if (j0 == 0 && jb == 0) {
 #pragma unroll
         for (int u = 0; u < JB; ++u) ob[u] = o0[u];
       } else {
 #pragma unroll
-        for (int u = 0; u < JB; ++u) ob[u] = jb + u < nj ? op[(int64_t)(j0 + jb + u) * D] : 0.f;
+        for (int u = 0; u < JB; ++u)
+          ob[u] = jb + u < nj ? op[(int64_t)(j0 + jb + u) * (D / DV)] : vdf{};
       }
 #pragma unroll
       for (int u = 0; u < JB; ++u) {
         if (jb + u >= nj) break;
-        const float w = sh_w[jb + u];
-        num += w * ob[u];
-        den += w * sh_l[jb + u];
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                      __builtin_bit_cast(int, wj), jb + u));
+        const float l = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                      __builtin_bit_cast(int, lj), jb + u));
+#pragma unroll
+        for (int d = 0; d < DV; ++d) num[d] += w * ob[u][d];
+        den += w * l;
       }
     }
   }
-  const float res = any_bad ? __builtin_nanf("") : num / den * A.v_scale;
-  A.out[((int64_t)(S.row_offset + r) * A.n_q_heads + h) * D + t] = f2bf(res);
+  uint16_t* dst = A.out + ((int64_t)(S.row_offset + r) * A.n_q_heads + h) * D + DV * lane;
+#pragma unroll
+  for (int d = 0; d < DV; ++d) dst[d] = f2bf(any_bad ? __builtin_nanf("") : num[d] / den * A.v_scale);
 }
 
 template <int KV, int D>
@@ -472,9 +460,9 @@ int launch_decode_partials(const DecodeArgs& A, int kv_dtype, int head_dim, int 
 int launch_decode_merge(const DecodeArgs& A, int head_dim, hipStream_t st) {
   dim3 grid((unsigned)A.total_rows, (unsigned)A.n_q_heads);
   if (head_dim == 128)
-    hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(128), 0, st, A);
+    hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(64), 0, st, A);
   else if (head_dim == 256)
-    hipLaunchKernelGGL((decode_merge_kernel<256>), grid, dim3(256), 0, st, A);
+    hipLaunchKernelGGL((decode_merge_kernel<256>), grid, dim3(64), 0, st, A);
   else
     return -7;
   return hipGetLastError() == hipSuccess ? 0 : -6;
