@@ -305,7 +305,7 @@ PROBE_BYTES = 8 << 30  # larger runs read faster: 6.25 / 6.21 / 6.44 / 6.63 TB/s
 def probe_abba(arm_a, a_bytes: int, launches: int = 10, rounds: int = 3) -> dict:
     """ABBA rounds of arm A (the decode partial kernel) against arm B, the
     library's plain streaming read of an 8 GiB buffer (pa_hbm_read_probe):
-    the box's achievable read rate, measured between the same launches."""
+    the device's achievable read rate, measured between the same launches."""
     import torch
 
     import paged_kv_cache_addressing_amd as pa
@@ -434,7 +434,7 @@ def cpu_baseline(wl, min_s: float = 10.0):
 
 def oracle_threads() -> int:
     """Threads the oracle runs on: the process's CPUs, at most 16 (one GPU's
-    share of the host on the boxes this runs on)."""
+    share of an eight-GPU host)."""
     return min(16, len(os.sched_getaffinity(0)))
 
 
