@@ -192,32 +192,41 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
 
   const float c = A.scale_log2;
   // Q^T operands (two E4M3 terms) of this wave's columns, and per column the
-  // logit scale c / sigma and the lag threshold in raw logit units.
-  // Q is loaded and split after the first K and V tiles are on their way
-  // (q_operands, called after the prologue's DMAs), so that a workgroup
-  // waits out one memory latency before its first step, not two.
+  // logit scale c / sigma and the lag threshold in raw logit units.  Q's
+  // loads go out first (q_load), beside the page ids and ancestor words,
+  // and are split into the operands (q_split) after the first K and V
+  // DMAs, so those loads' flight overlaps the page-table lookup and the
+  // tiles' flight.
   v8i qh[NTW][KK], ql[NTW][KK];
   float cc[NTW];
-  auto q_operands = [&]() __attribute__((always_inline)) {
+  // bytes 0..15 of k-step kk: dims 128kk + 16a + j; bytes 16..31: dims
+  // 128kk + 64 + 16a + j (four 16-byte loads of 8 bf16 each)
+  v4u qraw[NTW][KK][4];
+  auto q_load = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const Col k = col_of(qcol(nt));
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(A.q) +
+                          ((int64_t)(S.row_offset + (k.ok ? k.row : row0)) * A.n_q_heads +
+                           (k.ok ? k.head : h0)) * D * 2;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int q8 = 0; q8 < 2; ++q8)
+            qraw[nt][kk][2 * hf + q8] = load16(qp + (128 * kk + 64 * hf + 16 * a + 8 * q8) * 2);
+    }
+  };
+  auto q_split = [&]() __attribute__((always_inline)) {
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const Col k = col_of(qcol(nt));
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(A.q) +
-                        ((int64_t)(S.row_offset + (k.ok ? k.row : row0)) * A.n_q_heads +
-                         (k.ok ? k.head : h0)) * D * 2;
-    // bytes 0..15 of k-step kk: dims 128kk + 16a + j; bytes 16..31: dims
-    // 128kk + 64 + 16a + j (four 16-byte loads of 8 bf16 each)
     v4u raw[KK][4];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int q8 = 0; q8 < 2; ++q8) {
-          v4u x = load16(qp + (128 * kk + 64 * hf + 16 * a + 8 * q8) * 2);
-          if (!k.ok) x = v4u{0, 0, 0, 0};
-          raw[kk][2 * hf + q8] = x;
-        }
+      for (int j = 0; j < 4; ++j) raw[kk][j] = k.ok ? qraw[nt][kk][j] : v4u{0, 0, 0, 0};
     // element e (0, 1) of dword w (0..15) of k-step kk, as a float
     auto f32 = [&](int kk, int w, int e) {
       const uint32_t u = raw[kk][w >> 2][w & 3];
@@ -513,6 +522,18 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   };
 
   const int n_st = v_hi - v_lo;
+  // First the loads that do not wait on the page table: the item's page ids
+  // (for LDS), the ancestor words of this wave's columns, Q.
+  int32_t pid_l = 0;
+  if (wave == 0 && map.paged && t0 + lane <= t_last) pid_l = map.pt[t0 + lane];
+  uint32_t anc_l[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const Col k = col_of(qcol(nt));
+    anc_l[nt] = 0xFFFFFFFFu;
+    if (s == 0 && a == 0 && S.tree_mask && k.ok) anc_l[nt] = S.tree_mask[k.row];
+  }
+  q_load();
   if (v_hi > v_lo) {
     // Prologue DMAs, in the order the steady state expects: K(v_lo),
     // K(v_lo+1); then as "step v_lo-2" K(v_lo+2), V(v_lo), and as "step
@@ -525,15 +546,13 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
     if (n_st > 1) dma_v(v_lo + 1);
   }
   // Q operands, ancestor words and the page ids, while the first tiles load
-  q_operands();
+  q_split();
 #pragma unroll
   for (int j = 0; j < NPW; ++j) o[j] = v16f{};
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const Col k = col_of(qcol(nt));
-    if (s == 0 && a == 0) Anc[qcol(nt)] = (S.tree_mask && k.ok) ? S.tree_mask[k.row] : 0xFFFFFFFFu;
-  }
-  if (wave == 0 && map.paged) Pid[lane] = t0 + lane <= t_last ? map.pt[t0 + lane] : 0;
+  for (int nt = 0; nt < NTW; ++nt)
+    if (s == 0 && a == 0) Anc[qcol(nt)] = anc_l[nt];
+  if (wave == 0 && map.paged) Pid[lane] = pid_l;
 
   if (v_hi > v_lo) {
     // K(v_lo) and K(v_lo+1) landed: after them at most K(v_lo+2), V(v_lo),
@@ -631,8 +650,14 @@ __global__ __launch_bounds__(512, 1) void verify_kernel(const PrefillArgs A) {
   // partials: checked here, one id per lane, rather than carried through the
   // step loop.  (The tiles of such pages read page 0 instead.)
   bool bad_lane = false;
-  if (map.paged && v_hi > v_lo)
-    for (int t = t0 + lane; t <= t_last; t += 64) bad_lane |= (uint32_t)map.pt[t] >= (uint32_t)map.n_pages;
+  if (map.paged && v_hi > v_lo) {
+    if (t_last - t0 < 64) {
+      // the item's page ids are in LDS
+      if (lane <= t_last - t0) bad_lane = (uint32_t)Pid[lane] >= (uint32_t)map.n_pages;
+    } else {
+      for (int t = t0 + lane; t <= t_last; t += 64) bad_lane |= (uint32_t)map.pt[t] >= (uint32_t)map.n_pages;
+    }
+  }
   const bool bad = __any(bad_lane);
 
   // Row sums: each wave's partial over its keys (summed across the column's
