@@ -261,7 +261,12 @@ PA_API int write_kv(const pa_kv_cache *cache, const pa_stream *streams, int32_t 
  * n_rows per stream <= PA_DECODE_MAX_ROWS; sm_scale > 0 (1/sqrt(head_dim)
  * is the usual value); split_keys a positive multiple of 256.
  * The workspace (device, >= paged_attn_decode_workspace_size bytes, 256-byte
- * aligned) holds the partials; it is fully overwritten before it is read. */
+ * aligned) holds the partials; it is fully overwritten before it is read.
+ * When every stream of a launch group streams through registers and has a
+ * single split, the merge would weigh that split by exactly 1: the partial
+ * kernel then writes out (o / l * v_scale, in the merge's operation order,
+ * so the same bytes) and no merge runs; the group's workspace slots are not
+ * written. */
 PA_API size_t paged_attn_decode_workspace_size(const pa_stream *streams, int32_t n_streams,
                                         int32_t n_q_heads, int32_t head_dim, int32_t split_keys);
 

@@ -699,6 +699,17 @@ int paged_attn_decode(const pa_kv_cache* cache, const pa_stream* streams, int32_
                           workspace, workspace_bytes, true, true, L);
   if (rc != PA_OK) return rc;
   for (const auto& D : L) {
+    // A group whose streams all stream through registers with one split
+    // each needs no merge: its partial kernel writes the rows directly.
+    bool direct = D.wide.n_streams == 0 && D.narrow.n_streams > 0;
+    for (int32_t j = 0; direct && j < D.narrow.n_streams; ++j) direct = D.narrow.s[j].n_splits == 1;
+    if (direct) {
+      DecodeLaunch Dd = D;
+      Dd.narrow.direct_out = 1;
+      rc = launch_partials(Dd, cache, (hipStream_t)hip_stream);
+      if (rc != 0) return rc;
+      continue;
+    }
     rc = launch_partials(D, cache, (hipStream_t)hip_stream);
     if (rc != 0) return rc;
     rc = pa::launch_decode_merge(D.merge, cache->head_dim, (hipStream_t)hip_stream);

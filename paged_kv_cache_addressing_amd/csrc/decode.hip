@@ -33,7 +33,7 @@ __device__ __forceinline__ int qk_d(int ks, int a) {
   return KV ? (64 * (ks >> 1) + 16 * a + 8 * (ks & 1)) : (32 * ks + 8 * a);
 }
 
-template <int KV, int D>
+template <int KV, int D, bool DIRECT>
 __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs A) {
   constexpr int ESZ = KV ? 1 : 2;
   constexpr int KK = KV ? 2 : 1;      // 32-key PV k-steps per chunk
@@ -287,7 +287,19 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
         l_sum = l_sum * a0 + lw * aw;
         m_acc = M;
       }
-      if (col_ok) {
+      if constexpr (DIRECT) {
+        if (col_ok) {
+        // The call's only split: the merge would weigh it by 2^(m - m) = 1,
+        // so its result is o / l * v_scale, computed here in the merge's
+        // operation order (the same bytes) without the partials' round trip.
+          uint16_t* dst = A.out + ((int64_t)(S.row_offset + r) * A.n_q_heads + h) * D + 4 * a;
+#pragma unroll
+          for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              dst[16 * md + e] = f2bf(any_bad ? __builtin_nanf("") : o[md][e] / l_sum * A.v_scale);
+        }
+      } else if (col_ok) {
         const int64_t slot =
             S.slot_base + ((int64_t)r * A.n_q_heads + h) * S.n_splits + split0 + done;
         if (a == 0) {
@@ -444,7 +456,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs A) {
 template <int KV, int D>
 static int launch_partials_t(const DecodeArgs& A, int n_kv_heads, hipStream_t st) {
   dim3 grid((unsigned)(A.total_items * A.col_tiles), (unsigned)n_kv_heads);
-  hipLaunchKernelGGL((decode_partial_kernel<KV, D>), grid, dim3(256), 0, st, A);
+  // the direct-output form is its own instance, so the partial-writing one
+  // is compiled exactly as without it
+  if (A.direct_out)
+    hipLaunchKernelGGL((decode_partial_kernel<KV, D, true>), grid, dim3(256), 0, st, A);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<KV, D, false>), grid, dim3(256), 0, st, A);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

@@ -81,6 +81,7 @@ struct DecodeArgs {
   int32_t col_tiles;    // 16-column MFMA tiles per (split, kv head)
   int32_t total_rows;   // rows in this launch (merge grid)
   int32_t splits_per_wg;  // consecutive splits one workgroup computes
+  int32_t direct_out;   // 1: every stream has one split; write bf16 rows to out, no partials
   float scale_log2;     // sm_scale * k_scale * log2(e)
   float v_scale;
   StreamArg s[kMaxLaunchStreams];
