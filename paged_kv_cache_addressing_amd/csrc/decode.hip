@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   // flight stay in flight.  Wave 0 reads a set before it reaches the next
   // barrier, so the set is free again when the split after next ends.
   int done = 0;
-  auto boundary = [&]() {
+  auto boundary = [&]() __attribute__((always_inline)) {
     const int sp = done & 1;
     // Per-column row sum across the four lane groups, in a fixed order.
     float l_sum = rows4_sum(l_run);

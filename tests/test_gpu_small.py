@@ -114,6 +114,11 @@ DECODE_CASES = [
     # with one q head per kv head
     ("narrow-g8-d256", 32, 4, 256, "bf16", [7000, 300], [3, 2], None, 4096),
     ("mha-d256-fp8", 4, 4, 256, "fp8", [3000, 8193], [2, 1], ["slab", "paged"], 4096),
+    # every stream one split: the partial kernel writes the rows itself (no
+    # merge), at head_dim 256 for both KV dtypes
+    ("one-split-d256-bf16", 24, 4, 256, "bf16", [300, 4096, 1], [3, 1, 1], None, 4096),
+    ("one-split-d256-fp8", 24, 4, 256, "fp8", [4096, 2500, 2], [1, 2, 1],
+     ["paged", "slab", "paged"], 4096),
 ]
 
 
