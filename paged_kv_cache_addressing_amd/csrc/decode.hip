@@ -388,7 +388,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs A) {
   const int row = blockIdx.x;
   const int h = blockIdx.y;
   const int lane = threadIdx.x;
-  const int si = find_stream<1>(A.s, A.n_streams, row);
+  const int si = find_stream_wave<1>(A.s, A.n_streams, row);
   const StreamArg& S = A.s[si];
   const int r = row - S.row_begin;
   const int ns = S.n_splits;

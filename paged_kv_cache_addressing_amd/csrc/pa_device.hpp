@@ -245,23 +245,47 @@ __device__ __forceinline__ int find_stream(const StreamArg* s, int n, int x) {
   return si;
 }
 
+// The highest lane of the wave whose predicate holds, or 0 if none; the
+// result is wave-uniform.
+__device__ __forceinline__ int last_lane_where(bool p) {
+  const uint64_t m = __ballot(p);
+  return m ? 63 - __builtin_clzll(m) : 0;
+}
+
+// find_stream in one memory round trip, for kernels whose lookup is on the
+// critical path: lane i (1 <= i < n) reads stream i's begin with a vector
+// load, and the highest lane whose begin is <= x names the stream (0 if
+// none).  The loop above waits on each begin before reading the next.  Needs
+// the whole wave active.
+template <int FIELD>
+__device__ __forceinline__ int find_stream_wave(const StreamArg* s, int n, int x) {
+  static_assert(kMaxLaunchStreams <= 64, "one stream per lane");
+  const int lane = threadIdx.x & 63;
+  const int i = lane < n ? lane : 0;
+  const int b = FIELD == 0 ? s[i].block_begin : s[i].row_begin;
+  return last_lane_where(lane > 0 && lane < n && x >= b);
+}
+
 // Work item of a split-mode launch (decode streams with many columns),
 // workgroup L of nb: blocks [0, NH * F) are the whole splits (head group
 // major, then stream, row tile, split); the rest are the streams' shorter
 // last splits, longest first, all head groups of one before the next.  One
 // workgroup runs per compute unit, so this order decides the launch's tail.
-// hgrp = kv head * (group / heads_per_wg) + head group.
+// hgrp = kv head * (group / heads_per_wg) + head group.  The stream lookups
+// are wave-wide (one lane per stream), so the whole wave must be active.
 __device__ __forceinline__ void split_item(const PrefillArgs& A, int L, int nb, int& hgrp,
                                            int& si, int& tile, int& split) {
   const int rpt = A.rows_per_tile;
   const int NH = nb / A.total_tiles;
   const int F = A.full_tiles;
+  const int lane = threadIdx.x & 63;
+  const int i = lane < A.n_streams ? lane : 0;
   if (L < NH * F) {
     hgrp = L / F;
     const int r = L - hgrp * F;
-    si = 0;
-    for (int i = 1; i < A.n_streams; ++i)
-      if (r >= A.s[i].full_begin) si = i;
+    // the last stream whose whole splits begin at or before r; lane i tests
+    // stream i (one vector load for all streams)
+    si = last_lane_where(lane > 0 && lane < A.n_streams && r >= A.s[i].full_begin);
     const int nf = A.s[si].n_keys / A.split_keys;
     const int local = r - A.s[si].full_begin;
     tile = local / nf;
@@ -270,11 +294,10 @@ __device__ __forceinline__ void split_item(const PrefillArgs& A, int L, int nb, 
     const int j = L - NH * F;
     hgrp = j % NH;
     const int r = j / NH;
-    si = 0;
-    for (int i = 0; i < A.n_streams; ++i) {
-      const int pb = A.s[i].part_begin;
-      if (pb >= 0 && r >= pb && r < pb + (A.s[i].n_rows + rpt - 1) / rpt) si = i;
-    }
+    // the stream whose short last split's row tiles hold rank r
+    const int pb = A.s[i].part_begin;
+    si = last_lane_where(lane < A.n_streams && pb >= 0 && r >= pb &&
+                         r < pb + (A.s[i].n_rows + rpt - 1) / rpt);
     tile = r - A.s[si].part_begin;
     split = A.s[si].n_splits - 1;
   }

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const WriteArgs A) {
   constexpr int ESZ = KV ? 1 : 2;
   const int row = blockIdx.x;
   const int g = blockIdx.y;
-  const int si = find_stream<1>(A.s, A.n_streams, row);
+  const int si = find_stream_wave<1>(A.s, A.n_streams, row);
   const StreamArg& S = A.s[si];
   const int r = row - S.row_begin;
   const int pos = S.first_pos + r;
