@@ -45,9 +45,10 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
   constexpr int KL = KV ? MT * KS / 2 : MT * KS;  // 16-byte K loads per lane per chunk
 
   // Wave states at the end of a split, double-buffered by split parity.
-  __shared__ v4f sh_o[2][NW - 1][MD][64];
-  __shared__ float sh_m[2][NW - 1][64];
-  __shared__ float sh_l[2][NW - 1][64];
+  constexpr int MQ = MD / NW;  // O^T m-tiles each wave merges and writes
+  __shared__ v4f sh_o[2][NW][MD][64];
+  __shared__ float sh_m[2][NW][64];
+  __shared__ float sh_l[2][NW][64];
   __shared__ int sh_bad[2][NW];
 
   const int lane = threadIdx.x & 63;
@@ -251,65 +252,69 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeArgs
     }
   };
   // The end of split `done` of the workgroup: the waves' states go to the
-  // LDS set of its parity and, after a barrier, wave 0 merges them in fixed
-  // wave order and writes the partial; every wave then starts the next split
-  // afresh.  The barrier only orders LDS: loads of the next split already in
-  // flight stay in flight.  Wave 0 reads a set before it reaches the next
-  // barrier, so the set is free again when the split after next ends.
+  // LDS set of its parity and, after a barrier, each wave merges them in
+  // fixed wave order for a quarter of the dims and writes that quarter of the
+  // partial; every wave then starts the next split afresh.  Spreading the
+  // merge keeps the stores (which the next chunk's load wait also counts)
+  // and the merge arithmetic off a single wave.  The barrier only orders
+  // LDS: loads of the next split already in flight stay in flight.  A wave
+  // reads a set before it reaches the next barrier, so the set is free again
+  // when the split after next ends.
   int done = 0;
   auto boundary = [&]() __attribute__((always_inline)) {
     const int sp = done & 1;
     // Per-column row sum across the four lane groups, in a fixed order.
-    float l_sum = rows4_sum(l_run);
-    if (wave > 0) {
+    const float l_own = rows4_sum(l_run);
 #pragma unroll
-      for (int md = 0; md < MD; ++md) sh_o[sp][wave - 1][md][lane] = o[md];
-      sh_m[sp][wave - 1][lane] = m_run;
-      sh_l[sp][wave - 1][lane] = l_sum;
-    }
+    for (int md = 0; md < MD; ++md) sh_o[sp][wave][md][lane] = o[md];
+    sh_m[sp][wave][lane] = m_run;
+    sh_l[sp][wave][lane] = l_own;
     if (lane == 0) sh_bad[sp][wave] = bad ? 1 : 0;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (wave == 0) {
-      bool any_bad = false;
+    bool any_bad = false;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) any_bad |= sh_bad[sp][w] != 0;
-      // Merge waves 1..NW-1 into wave 0 in fixed order.
-      float m_acc = m_run;
-      for (int w = 1; w < NW; ++w) {
-        const float mw = sh_m[sp][w - 1][lane];
-        const float lw = sh_l[sp][w - 1][lane];
-        const float M = fmaxf(m_acc, mw);
-        if (M == -INFINITY) continue;
-        const float a0 = __builtin_amdgcn_exp2f(m_acc - M);
-        const float aw = __builtin_amdgcn_exp2f(mw - M);
+    for (int w = 0; w < NW; ++w) any_bad |= sh_bad[sp][w] != 0;
+    // Merge the waves in fixed order 0, 1, .., NW-1; this wave takes the
+    // O^T m-tiles MQ*wave .. MQ*wave+MQ-1, every wave the same (m, l).
+    float m_acc = sh_m[sp][0][lane];
+    float l_sum = sh_l[sp][0][lane];
+    v4f acc[MQ];
 #pragma unroll
-        for (int md = 0; md < MD; ++md) o[md] = o[md] * a0 + sh_o[sp][w - 1][md][lane] * aw;
-        l_sum = l_sum * a0 + lw * aw;
-        m_acc = M;
-      }
-      if constexpr (DIRECT) {
-        if (col_ok) {
+    for (int j = 0; j < MQ; ++j) acc[j] = sh_o[sp][0][MQ * wave + j][lane];
+    for (int w = 1; w < NW; ++w) {
+      const float mw = sh_m[sp][w][lane];
+      const float lw = sh_l[sp][w][lane];
+      const float M = fmaxf(m_acc, mw);
+      if (M == -INFINITY) continue;
+      const float a0 = __builtin_amdgcn_exp2f(m_acc - M);
+      const float aw = __builtin_amdgcn_exp2f(mw - M);
+#pragma unroll
+      for (int j = 0; j < MQ; ++j) acc[j] = acc[j] * a0 + sh_o[sp][w][MQ * wave + j][lane] * aw;
+      l_sum = l_sum * a0 + lw * aw;
+      m_acc = M;
+    }
+    if constexpr (DIRECT) {
+      if (col_ok) {
         // The call's only split: the merge would weigh it by 2^(m - m) = 1,
         // so its result is o / l * v_scale, computed here in the merge's
         // operation order (the same bytes) without the partials' round trip.
-          uint16_t* dst = A.out + ((int64_t)(S.row_offset + r) * A.n_q_heads + h) * D + 4 * a;
+        uint16_t* dst = A.out + ((int64_t)(S.row_offset + r) * A.n_q_heads + h) * D + 4 * a;
 #pragma unroll
-          for (int md = 0; md < MD; ++md)
+        for (int j = 0; j < MQ; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              dst[16 * md + e] = f2bf(any_bad ? __builtin_nanf("") : o[md][e] / l_sum * A.v_scale);
-        }
-      } else if (col_ok) {
-        const int64_t slot =
-            S.slot_base + ((int64_t)r * A.n_q_heads + h) * S.n_splits + split0 + done;
-        if (a == 0) {
-          A.ws_ml[2 * slot] = any_bad ? __builtin_nanf("") : m_acc;
-          A.ws_ml[2 * slot + 1] = l_sum;
-        }
-        float* dst = A.ws_o + slot * D + 4 * a;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) *reinterpret_cast<v4f*>(dst + 16 * md) = o[md];
+          for (int e = 0; e < 4; ++e)
+            dst[16 * (MQ * wave + j) + e] = f2bf(any_bad ? __builtin_nanf("") : acc[j][e] / l_sum * A.v_scale);
       }
+    } else if (col_ok) {
+      const int64_t slot =
+          S.slot_base + ((int64_t)r * A.n_q_heads + h) * S.n_splits + split0 + done;
+      if (wave == 0 && a == 0) {
+        A.ws_ml[2 * slot] = any_bad ? __builtin_nanf("") : m_acc;
+        A.ws_ml[2 * slot + 1] = l_sum;
+      }
+      float* dst = A.ws_o + slot * D + 4 * a;
+#pragma unroll
+      for (int j = 0; j < MQ; ++j) *reinterpret_cast<v4f*>(dst + 16 * (MQ * wave + j)) = acc[j];
     }
 #pragma unroll
     for (int md = 0; md < MD; ++md) o[md] = v4f{0.f, 0.f, 0.f, 0.f};
